@@ -1,0 +1,173 @@
+/*
+ * sparse_topk.h -- C ABI of the indexer top-k selection library for MI355X (gfx950).
+ *
+ * What the library computes
+ * -------------------------
+ * The lmsys.org page "Serving GLM5.2 NVFP4 Agentic Workload with SGLang",
+ * section "Kernel Optimization / TopK-V2" (text and the captions of Figures 2,
+ * 3 and 4), describes the DSA indexer's top-k step: each query row holds FP32
+ * scores over historical KV positions; the kernel returns exactly k of those
+ * positions (runtime k up to 2048), decided exactly at the FP32 boundary with
+ * an exact tie-break, and translates every selected logical position into a
+ * physical indexer-KV-cache slot through the paged block table, in the same
+ * kernel. A planning kernel, run once per forward and reused across indexer
+ * layers, turns the batch's length distribution into a work list.
+ *
+ * For row r with n = lengths[r] valid scores the selected set is
+ *     the first min(k, n) positions of [0, n) ordered by
+ *     (score descending, position ascending),
+ * i.e. ties at equal score go to the lower logical position (the page does not
+ * print the tie rule; this is the reading the library implements). -0.0 and
+ * +0.0 are equal scores; -inf is an ordinary lowest score. Positions >= n are
+ * never read as candidates, whatever they hold.
+ * Selected position i maps to slot  block_table[r * bt_row_stride + i / page_size]
+ *                                    * page_size + i % page_size.
+ *
+ * Output of a row: entries [0, min(k, n)) hold the selected positions' slots in
+ * UNSPECIFIED order (the page treats top-k as selection, not sorting); entries
+ * [min(k, n), k) hold -1. When out_indices is given, out_indices[r][j] is the
+ * logical position whose slot is out_slots[r][j].
+ *
+ * Memory and threading
+ * --------------------
+ * All data pointers are DEVICE pointers unless a parameter says "host". All
+ * work is enqueued asynchronously on `stream` (a hipStream_t passed as void*;
+ * NULL means the default stream). The caller owns every buffer. topk_plan and
+ * topk_select_paged never allocate, free or synchronise, so both may be
+ * captured into a HIP graph. A workspace must not be used by two calls that
+ * can run at the same time.
+ *
+ * Errors
+ * ------
+ * Host-checkable argument errors are returned synchronously and nothing is
+ * enqueued. Violations of the device-data contract below cannot be checked
+ * without a synchronisation; results are then undefined, and a device status
+ * word in the workspace may record them (topk_read_status):
+ *   0 <= lengths[r] <= max_len and <= score_row_stride;
+ *   no NaN among the valid scores;
+ *   the block table covers ceil(lengths[r] / page_size) pages with entries >= 0,
+ *   and every slot page * page_size + page_size - 1 fits in int32;
+ *   the lengths given to topk_select_paged equal those the plan was built from.
+ */
+#ifndef SPARSE_TOPK_H
+#define SPARSE_TOPK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TOPK_OK = 0,
+  TOPK_ERR_INVALID_ARG = -1,     /* a host-checkable argument is out of range or NULL */
+  TOPK_ERR_BUFFER_TOO_SMALL = -2,/* plan or workspace smaller than topk_query_sizes says */
+  TOPK_ERR_UNSUPPORTED = -3,     /* forced path cannot serve the configured rows */
+  TOPK_ERR_HIP = -4,             /* a HIP runtime call or kernel launch failed */
+  TOPK_ERR_DEVICE = -5           /* topk_read_status: the device recorded an error */
+} topk_status;
+
+/* Path selection (tests and tuning). AUTO lets the planner choose per row. */
+enum {
+  TOPK_PATH_AUTO = 0,
+  TOPK_PATH_REGISTER = 1,  /* one workgroup per row, row held in registers (len <= topk_register_capacity()) */
+  TOPK_PATH_SINGLE = 2,    /* one workgroup per row, streamed */
+  TOPK_PATH_MULTI = 3      /* every row longer than k split across workgroups */
+};
+
+/* Host struct, read through the pointer and never retained. */
+typedef struct {
+  int32_t k;              /* 1 .. 2048 */
+  int32_t max_rows;       /* rows the plan and workspace are sized for (>= 1) */
+  int64_t max_len;        /* largest valid length of any row (>= 0, < 2^31) */
+  int32_t force_path;     /* TOPK_PATH_* */
+  int32_t wg_per_row;     /* 0 = planner's choice; > 0 fixes the workgroups per split row */
+  int32_t cand_capacity;  /* 0 = default; > 0 caps the per-row boundary-candidate buffer
+                             (rows whose boundary bin holds more use a re-streaming path) */
+  int32_t min_chunk;      /* 0 = default; > 0 smallest chunk (elements) the planner splits to */
+  int32_t reserved[4];    /* must be zero */
+} topk_config;
+
+/*
+ * Host only. Sizes in bytes of the plan buffer (written by topk_plan) and the
+ * workspace (used by topk_select_paged) for `cfg` on the current HIP device.
+ * Status: OK, INVALID_ARG (bad cfg or NULL outputs), HIP (device query failed).
+ */
+topk_status topk_query_sizes(const topk_config* cfg, size_t* plan_bytes, size_t* workspace_bytes);
+
+/*
+ * Enqueue a fill kernel that zeroes `workspace`. Required once before the
+ * first topk_select_paged on a workspace, and again after topk_read_status
+ * reports TOPK_ERR_DEVICE. topk_select_paged leaves the workspace zeroed for
+ * the next call, so no per-call clearing is needed (or recorded in a graph).
+ */
+topk_status topk_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The planning step (page: TopK-V2, paragraph on the planning kernel): a
+ * device kernel reads `lengths` (int32[num_rows], device) and writes the work
+ * list into `plan`. Run it once per forward; the plan stays valid for any
+ * number of topk_select_paged calls whose lengths are the same values.
+ * 0 <= num_rows <= cfg->max_rows. No host synchronisation.
+ */
+topk_status topk_plan(const topk_config* cfg, const int32_t* lengths, int32_t num_rows,
+                      void* plan, size_t plan_bytes, void* stream);
+
+/*
+ * The fused selection and page-table transform (page: TopK-V2, Figures 2-4).
+ *   scores          float[num_rows][score_row_stride], row-major; row r's valid
+ *                   prefix is lengths[r]. score_row_stride >= cfg->max_len.
+ *   block_table     int32; row r's table starts at block_table + r * bt_row_stride
+ *                   (bt_row_stride == 0: one table shared by all rows).
+ *   page_size       tokens per KV page, >= 1.
+ *   out_slots       int32[num_rows][out_row_stride], out_row_stride >= k.
+ *   out_indices     int32[num_rows][out_row_stride] or NULL.
+ *   plan            written by topk_plan for the same cfg and lengths.
+ *   workspace       >= topk_query_sizes bytes, zeroed once by topk_workspace_init.
+ * Status: OK, INVALID_ARG, BUFFER_TOO_SMALL, UNSUPPORTED, HIP. No host synchronisation.
+ */
+topk_status topk_select_paged(const topk_config* cfg, const void* plan,
+                              const float* scores, int64_t score_row_stride,
+                              const int32_t* lengths, int32_t num_rows,
+                              const int32_t* block_table, int64_t bt_row_stride,
+                              int32_t page_size,
+                              int32_t* out_slots, int32_t* out_indices, int64_t out_row_stride,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * SYNCHRONISES `stream`. Copies the device status word of `workspace` into
+ * *host_status (host pointer): 0, or a bitwise OR of TOPK_DEVICE_* flags.
+ * Returns TOPK_ERR_DEVICE when the word is non-zero.
+ */
+enum {
+  TOPK_DEVICE_SPIN_TIMEOUT = 1,  /* workgroups of a split row never all arrived */
+  TOPK_DEVICE_PLAN_MISMATCH = 2, /* plan built for another k or never written */
+  TOPK_DEVICE_BAD_LENGTH = 4,    /* a length outside [0, max_len] */
+  TOPK_DEVICE_INTERNAL = 8       /* an internal consistency check failed */
+};
+topk_status topk_read_status(const void* workspace, size_t workspace_bytes,
+                             int32_t* host_status, void* stream);
+
+/* Elements one workgroup holds in registers (the register path's row limit). */
+int64_t topk_register_capacity(void);
+
+/*
+ * Test hook for the key transform of the page's Figure 3 caption (FP32 score
+ * rounded to FP16, mapped to an unsigned key ordered like the score; the top
+ * 10 key bits select one of 1,024 bins). For each x[i] (device, n >= 0) it
+ * writes what the selection kernel itself computes:
+ *   bin_out[i]   = histogram bin of x[i], 0..1023 (-0.0 shares +0.0's bin)
+ *   key32_out[i] = order-preserving unsigned key of the FP32 value of x[i]
+ *                  (-0.0 shares +0.0's key), used by the exact refinement
+ * Either output pointer may be NULL. Enqueued on `stream`.
+ */
+topk_status topk_debug_keys(const float* x, int64_t n, uint32_t* bin_out, uint32_t* key32_out, void* stream);
+
+const char* topk_status_string(topk_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_TOPK_H */

@@ -1,0 +1,214 @@
+// topk_api.hip -- C ABI of the indexer top-k library: argument checks, buffer
+// sizing and kernel launches. No allocation and no synchronisation happen
+// here except in topk_read_status, which says so.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+#include "sparse_topk.h"
+#include "topk_layout.hpp"
+
+namespace satopk {
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_select(const SelectArgs& a, int grid, bool vec, hipStream_t s);
+hipError_t launch_fill(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_debug_keys(const float* x, int64_t n, uint32_t* bin, uint32_t* k32, hipStream_t s);
+hipError_t select_occupancy(int* per_cu);
+}  // namespace satopk
+
+using namespace satopk;
+
+namespace {
+
+// Per-device CU count and co-resident selection workgroups per CU. This cache
+// is the library's only global state; it never changes once filled.
+struct DevInfo {
+  int cus = 0;
+  int per_cu = 0;
+  bool ready = false;
+};
+constexpr int kMaxDevices = 64;
+DevInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+topk_status device_info(DevInfo* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TOPK_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  DevInfo& d = g_dev[dev];
+  if (!d.ready) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return TOPK_ERR_HIP;
+    int per_cu = 0;
+    if (select_occupancy(&per_cu) != hipSuccess || per_cu <= 0) return TOPK_ERR_HIP;
+    d.cus = cus;
+    d.per_cu = per_cu;
+    d.ready = true;
+  }
+  *out = d;
+  return TOPK_OK;
+}
+
+topk_status check_config(const topk_config* cfg) {
+  if (!cfg) return TOPK_ERR_INVALID_ARG;
+  if (cfg->k < 1 || cfg->k > kMaxK) return TOPK_ERR_INVALID_ARG;
+  if (cfg->max_rows < 1) return TOPK_ERR_INVALID_ARG;
+  if (cfg->max_len < 0 || cfg->max_len > 0x7FFFFFFFLL) return TOPK_ERR_INVALID_ARG;
+  if (cfg->force_path < TOPK_PATH_AUTO || cfg->force_path > TOPK_PATH_MULTI) return TOPK_ERR_INVALID_ARG;
+  if (cfg->wg_per_row < 0 || cfg->wg_per_row == 1) return TOPK_ERR_INVALID_ARG;
+  if (cfg->cand_capacity < 0 || cfg->min_chunk < 0) return TOPK_ERR_INVALID_ARG;
+  for (int i = 0; i < 4; ++i)
+    if (cfg->reserved[i] != 0) return TOPK_ERR_INVALID_ARG;
+  if (cfg->force_path == TOPK_PATH_REGISTER && cfg->max_len > kTile) return TOPK_ERR_UNSUPPORTED;
+  return TOPK_OK;
+}
+
+topk_status sizing(const topk_config* cfg, Sizing* s) {
+  topk_status st = check_config(cfg);
+  if (st != TOPK_OK) return st;
+  DevInfo d;
+  st = device_info(&d);
+  if (st != TOPK_OK) return st;
+  s->grid = d.cus * d.per_cu;
+  s->max_items = s->grid + cfg->max_rows;
+  int groups = s->grid / 2;
+  if (groups > cfg->max_rows) groups = cfg->max_rows;
+  if (groups < 1) groups = 1;
+  s->max_groups = groups;
+  int64_t cap = cfg->cand_capacity > 0 ? cfg->cand_capacity
+                                       : (cfg->max_len < kDefaultCandCap ? cfg->max_len : kDefaultCandCap);
+  s->cand_cap = cap < 1 ? 1 : cap;
+  const bool splits = cfg->force_path == TOPK_PATH_AUTO || cfg->force_path == TOPK_PATH_MULTI;
+  if (splits && cfg->wg_per_row > 0) {
+    // a fixed group size must fit one grid round for every row at once
+    if ((int64_t)cfg->wg_per_row * cfg->max_rows > s->grid || cfg->max_rows > s->max_groups)
+      return TOPK_ERR_UNSUPPORTED;
+  }
+  s->plan_bytes = sizeof(PlanHeader) + sizeof(WorkItem) * (size_t)s->max_items;
+  s->workspace_bytes = ws_total_bytes(*s);
+  return TOPK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+topk_status topk_query_sizes(const topk_config* cfg, size_t* plan_bytes, size_t* workspace_bytes) {
+  if (!plan_bytes || !workspace_bytes) return TOPK_ERR_INVALID_ARG;
+  Sizing s;
+  const topk_status st = sizing(cfg, &s);
+  if (st != TOPK_OK) return st;
+  *plan_bytes = s.plan_bytes;
+  *workspace_bytes = s.workspace_bytes;
+  return TOPK_OK;
+}
+
+topk_status topk_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace || workspace_bytes % 4 != 0) return TOPK_ERR_INVALID_ARG;
+  return launch_fill(workspace, workspace_bytes, (hipStream_t)stream) == hipSuccess ? TOPK_OK : TOPK_ERR_HIP;
+}
+
+topk_status topk_plan(const topk_config* cfg, const int32_t* lengths, int32_t num_rows, void* plan,
+                      size_t plan_bytes, void* stream) {
+  Sizing s;
+  const topk_status st = sizing(cfg, &s);
+  if (st != TOPK_OK) return st;
+  if (num_rows < 0 || num_rows > cfg->max_rows || !plan) return TOPK_ERR_INVALID_ARG;
+  if (num_rows > 0 && !lengths) return TOPK_ERR_INVALID_ARG;
+  if (plan_bytes < s.plan_bytes) return TOPK_ERR_BUFFER_TOO_SMALL;
+  if (num_rows == 0) return TOPK_OK;
+  const bool no_split = cfg->force_path == TOPK_PATH_REGISTER || cfg->force_path == TOPK_PATH_SINGLE;
+  PlanArgs a;
+  a.lengths = lengths;
+  a.num_rows = num_rows;
+  a.k = cfg->k;
+  a.grid = s.grid;
+  a.max_groups = s.max_groups;
+  a.max_items = s.max_items;
+  a.force_path = cfg->force_path;
+  a.wg_per_row = no_split ? 0 : cfg->wg_per_row;
+  a.min_chunk = cfg->min_chunk;
+  a.max_len = cfg->max_len;
+  a.header = (PlanHeader*)plan;
+  a.items = (WorkItem*)((char*)plan + sizeof(PlanHeader));
+  return launch_plan(a, (hipStream_t)stream) == hipSuccess ? TOPK_OK : TOPK_ERR_HIP;
+}
+
+topk_status topk_select_paged(const topk_config* cfg, const void* plan, const float* scores,
+                              int64_t score_row_stride, const int32_t* lengths, int32_t num_rows,
+                              const int32_t* block_table, int64_t bt_row_stride, int32_t page_size,
+                              int32_t* out_slots, int32_t* out_indices, int64_t out_row_stride, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  Sizing s;
+  const topk_status st = sizing(cfg, &s);
+  if (st != TOPK_OK) return st;
+  if (num_rows < 0 || num_rows > cfg->max_rows) return TOPK_ERR_INVALID_ARG;
+  if (page_size < 1 || bt_row_stride < 0 || out_row_stride < cfg->k) return TOPK_ERR_INVALID_ARG;
+  if (score_row_stride < cfg->max_len || score_row_stride < 0) return TOPK_ERR_INVALID_ARG;
+  if (!plan || !workspace) return TOPK_ERR_INVALID_ARG;
+  if (num_rows > 0 && (!scores || !lengths || !block_table || !out_slots)) return TOPK_ERR_INVALID_ARG;
+  if (workspace_bytes < s.workspace_bytes) return TOPK_ERR_BUFFER_TOO_SMALL;
+  if (num_rows == 0) return TOPK_OK;
+  SelectArgs a;
+  a.scores = scores;
+  a.stride = score_row_stride;
+  a.lengths = lengths;
+  a.num_rows = num_rows;
+  a.k = cfg->k;
+  a.table = block_table;
+  a.table_stride = bt_row_stride;
+  a.page_size = page_size;
+  a.page_shift = -1;
+  if ((page_size & (page_size - 1)) == 0) {
+    int sh = 0;
+    while ((1 << sh) < page_size) ++sh;
+    a.page_shift = sh;
+  }
+  a.out_slots = out_slots;
+  a.out_idx = out_indices;
+  a.out_stride = out_row_stride;
+  a.plan = (const PlanHeader*)plan;
+  a.items = (const WorkItem*)((const char*)plan + sizeof(PlanHeader));
+  a.groups = (GroupState*)((char*)workspace + ws_group_offset());
+  a.cand = (uint64_t*)((char*)workspace + ws_cand_offset(s));
+  a.cand_cap = s.cand_cap;
+  a.status = (int32_t*)workspace;
+  a.max_len = cfg->max_len;
+  a.spin_limit = kDefaultSpinLimit;
+  const bool vec = ((uintptr_t)scores % 16 == 0) && (score_row_stride % 4 == 0);
+  return launch_select(a, s.grid, vec, (hipStream_t)stream) == hipSuccess ? TOPK_OK : TOPK_ERR_HIP;
+}
+
+topk_status topk_read_status(const void* workspace, size_t workspace_bytes, int32_t* host_status, void* stream) {
+  if (!workspace || !host_status || workspace_bytes < kStatusBytes) return TOPK_ERR_INVALID_ARG;
+  int32_t v = 0;
+  if (hipMemcpyAsync(&v, workspace, sizeof(v), hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess)
+    return TOPK_ERR_HIP;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return TOPK_ERR_HIP;
+  *host_status = v;
+  return v ? TOPK_ERR_DEVICE : TOPK_OK;
+}
+
+int64_t topk_register_capacity(void) { return kTile; }
+
+topk_status topk_debug_keys(const float* x, int64_t n, uint32_t* bin_out, uint32_t* key32_out, void* stream) {
+  if (n < 0 || (n > 0 && !x)) return TOPK_ERR_INVALID_ARG;
+  return launch_debug_keys(x, n, bin_out, key32_out, (hipStream_t)stream) == hipSuccess
+             ? TOPK_OK
+             : TOPK_ERR_HIP;
+}
+
+const char* topk_status_string(topk_status s) {
+  switch (s) {
+    case TOPK_OK: return "ok";
+    case TOPK_ERR_INVALID_ARG: return "invalid argument";
+    case TOPK_ERR_BUFFER_TOO_SMALL: return "plan or workspace buffer too small";
+    case TOPK_ERR_UNSUPPORTED: return "forced path cannot serve this configuration";
+    case TOPK_ERR_HIP: return "HIP runtime error";
+    case TOPK_ERR_DEVICE: return "device recorded an error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

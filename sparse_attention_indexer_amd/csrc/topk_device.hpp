@@ -1,0 +1,121 @@
+// topk_device.hpp -- gfx950 device helpers of the indexer top-k library:
+// ordered keys, wave64 primitives, block scans and LDS histograms.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "topk_layout.hpp"
+
+namespace satopk {
+
+// ---------------------------------------------------------------------------
+// Ordered keys. The lmsys.org TopK-V2 section (Figure 3 caption) maps each
+// score to an unsigned key ordered like the score: flip all bits of a
+// negative value, set the sign bit of a non-negative one, which turns
+// sign-magnitude order into unsigned order. -0.0 is first replaced by +0.0 (a
+// test on the bit pattern, so no denormal is flushed) because the two scores
+// are equal and must share a key. This FP32 key drives the exact boundary
+// refinement; the FP16 histogram key lives with the selection kernel.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t canon_bits(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return b == 0x80000000u ? 0u : b;
+}
+
+__device__ __forceinline__ uint32_t key32_of(float x) {
+  const uint32_t b = canon_bits(x);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// ---------------------------------------------------------------------------
+// wave64 primitives
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t lane() { return __lane_id(); }
+
+__device__ __forceinline__ uint32_t mbcnt(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ uint32_t first_lane(uint64_t m) {
+  return (uint32_t)__builtin_ctzll(m);
+}
+
+__device__ __forceinline__ uint32_t read_lane(uint32_t v, uint32_t l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, (int)l);
+}
+
+__device__ __forceinline__ uint32_t wave_inclusive_add(uint32_t x) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(x, (unsigned)d, 64);
+    if (lane() >= (uint32_t)d) x += y;
+  }
+  return x;
+}
+
+// Exclusive prefix sum over the workgroup in thread order. `scratch` holds
+// kWaves words of LDS. Every thread must call it.
+__device__ __forceinline__ uint32_t block_exclusive_add(uint32_t x, uint32_t* scratch,
+                                                        uint32_t* total = nullptr) {
+  const uint32_t w = threadIdx.x >> 6;
+  const uint32_t inc = wave_inclusive_add(x);
+  if (lane() == 63) scratch[w] = inc;
+  __syncthreads();
+  uint32_t pre = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    const uint32_t s = scratch[i];
+    pre += ((uint32_t)i < w) ? s : 0u;
+    tot += s;
+  }
+  __syncthreads();
+  if (total) *total = tot;
+  return pre + inc - x;
+}
+
+// LDS histogram increment, aggregated per wave: when every active lane hits
+// the same bin (all-equal or one-bin rows) one atomic adds the lane count
+// instead of 64 conflicting atomics. Must be called by the whole wave.
+__device__ __forceinline__ void hist_add(uint32_t* h, bool m, uint32_t bin) {
+  const uint64_t act = __ballot(m);
+  if (act == 0) return;
+  const uint32_t leader = first_lane(act);
+  const uint32_t b0 = read_lane(bin, leader);
+  const uint64_t same = __ballot(m && bin == b0);
+  if (same == act) {
+    if (lane() == leader) atomicAdd(&h[b0], (uint32_t)__popcll(act));
+  } else if (m) {
+    atomicAdd(&h[bin], 1u);
+  }
+}
+
+// Scan `nb` bins from the top and find the bin holding the need-th largest
+// element: above(b) < need <= above(b) + h[b]. Writes (b, above(b), h[b]) to
+// result[0..2]. PB bins per thread; nb <= PB * kBlock; 1 <= need <= sum(h).
+template <int PB>
+__device__ __forceinline__ void find_threshold(const uint32_t* hist, int nb, uint32_t need,
+                                               uint32_t* scratch, uint32_t* result) {
+  const int t = threadIdx.x;
+  uint32_t h[PB];
+  uint32_t s = 0;
+#pragma unroll
+  for (int j = 0; j < PB; ++j) {
+    const int b = nb - 1 - (t * PB + j);
+    h[j] = b >= 0 ? hist[b] : 0u;
+    s += h[j];
+  }
+  uint32_t cum = block_exclusive_add(s, scratch);
+#pragma unroll
+  for (int j = 0; j < PB; ++j) {
+    const int b = nb - 1 - (t * PB + j);
+    if (cum < need && need <= cum + h[j]) {
+      result[0] = (uint32_t)b;
+      result[1] = cum;
+      result[2] = h[j];
+    }
+    cum += h[j];
+  }
+  __syncthreads();
+}
+
+}  // namespace satopk

@@ -1,0 +1,122 @@
+// topk_layout.hpp -- tile sizes, plan and workspace layouts shared by the host
+// launcher and the gfx950 kernels of the indexer top-k library.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace satopk {
+
+// Workgroup shape. 512 lanes = 8 wave64s; every lane holds kEpt scores of a
+// register-resident tile (kEpt / 4 dwordx4 loads in flight per lane).
+constexpr int kBlock = 512;
+constexpr int kWaves = kBlock / 64;
+constexpr int kEpt = 32;
+constexpr int kTile = kBlock * kEpt;          // 16,384 scores = 64 KB per tile
+
+constexpr int kMaxK = 2048;
+constexpr int kBins = 1024;                   // top 10 bits of the 16-bit ordered key
+constexpr int kRadixBits = 11;                // digit width of the exact refinement
+constexpr int kRadixBins = 1 << kRadixBits;
+constexpr int kListCap = 4096;                // boundary survivors kept in LDS
+constexpr int kChunkAlign = 256;              // chunk starts are multiples of this
+constexpr int kDefaultMinChunk = 4096;
+constexpr int kDefaultCandCap = 16384;        // boundary candidates per split row
+
+constexpr uint32_t kPlanMagic = 0x31504B54u;  // "TKP1"
+constexpr uint32_t kDefaultSpinLimit = 1u << 21;
+
+// Plan buffer: header, then `capacity` work items.
+struct PlanHeader {
+  uint32_t magic;
+  int32_t num_rows;
+  int32_t num_items;        // items actually written
+  int32_t num_multi_items;  // items [0, num_multi_items) belong to split rows
+  int32_t grid;             // workgroups the selection launch uses
+  int32_t k;
+  int32_t num_groups;       // split rows (each owns one GroupState)
+  int32_t chunk;            // planner's target chunk (diagnostic)
+  int32_t pad[8];
+};
+static_assert(sizeof(PlanHeader) == 64, "plan header is 64 bytes");
+
+struct WorkItem {
+  int32_t row;
+  int32_t begin;   // chunk [begin, end) of the row
+  int32_t end;
+  int32_t group;   // -1: the workgroup owns the whole row; else split-row slot
+  int32_t gsize;   // workgroups sharing the row (1 for an owned row)
+  int32_t pad[3];
+};
+static_assert(sizeof(WorkItem) == 32, "work item is 32 bytes");
+
+// Cross-workgroup state of one split row. Left zeroed after every use.
+struct GroupState {
+  uint32_t hist[kBins];   // merged 1,024-bin histogram
+  uint32_t arrive;        // workgroups that merged their histogram
+  uint32_t emit;          // output cursor for scores above the threshold bin
+  uint32_t cand;          // cursor into this row's candidate buffer
+  uint32_t done;          // workgroups that finished emission
+  uint32_t range[4];      // threshold-bin candidates: max key32, ~min key32, max pos, ~min pos
+  uint32_t pad[8];
+};
+static_assert(sizeof(GroupState) == 4096 + 64, "group state layout");
+
+// The device status word sits at workspace offset 0.
+constexpr size_t kStatusBytes = 256;
+
+struct Sizing {
+  int grid;          // persistent selection grid (<= co-resident capacity)
+  int max_items;     // plan capacity in items
+  int max_groups;    // split rows the workspace can hold
+  int64_t cand_cap;  // candidates per split row
+  size_t plan_bytes;
+  size_t workspace_bytes;
+};
+
+// Workspace: [status, kStatusBytes][GroupState x max_groups][uint64 cand x max_groups x cand_cap]
+inline size_t ws_group_offset() { return kStatusBytes; }
+inline size_t ws_cand_offset(const Sizing& s) { return kStatusBytes + sizeof(GroupState) * (size_t)s.max_groups; }
+inline size_t ws_total_bytes(const Sizing& s) {
+  return ws_cand_offset(s) + sizeof(uint64_t) * (size_t)s.max_groups * (size_t)s.cand_cap;
+}
+
+struct PlanArgs {
+  const int32_t* lengths;
+  int32_t num_rows;
+  int32_t k;
+  int32_t grid;
+  int32_t max_groups;
+  int32_t max_items;
+  int32_t force_path;
+  int32_t wg_per_row;
+  int32_t min_chunk;
+  int64_t max_len;
+  PlanHeader* header;
+  WorkItem* items;
+};
+
+struct SelectArgs {
+  const float* scores;
+  int64_t stride;
+  const int32_t* lengths;
+  int32_t num_rows;
+  int32_t k;
+  const int32_t* table;
+  int64_t table_stride;
+  int32_t page_size;
+  int32_t page_shift;     // log2(page_size) when a power of two, else -1
+  int32_t* out_slots;
+  int32_t* out_idx;       // may be null
+  int64_t out_stride;
+  const PlanHeader* plan;
+  const WorkItem* items;
+  GroupState* groups;
+  uint64_t* cand;
+  int64_t cand_cap;
+  int32_t* status;
+  int64_t max_len;
+  uint32_t spin_limit;
+};
+
+}  // namespace satopk

@@ -1,0 +1,104 @@
+"""The C ABI library on the CPU: it loads, exports every declared symbol, and
+rejects host-checkable bad arguments before touching the (absent) GPU."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_topk.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(topk_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def T():
+    from sparse_attention_indexer_amd import topk
+    topk.load_library()
+    return topk
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("topk_query_sizes", "topk_plan", "topk_select_paged", "topk_workspace_init",
+              "topk_read_status", "topk_status_string", "topk_register_capacity", "topk_debug_keys"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(T):
+    lib = T.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(T):
+    lib = T.load_library()
+    for st in (0, -1, -2, -3, -4, -5):
+        assert lib.topk_status_string(st)
+    assert lib.topk_status_string(-99) == b"unknown status"
+
+
+def test_register_capacity(T):
+    assert T.topk_register_capacity() == 16384
+
+
+@pytest.mark.parametrize("kw", [
+    dict(k=0), dict(k=2049), dict(max_rows=0), dict(max_len=-1), dict(max_len=1 << 31),
+    dict(force_path=4), dict(force_path=-1), dict(wg_per_row=1), dict(wg_per_row=-2),
+    dict(cand_capacity=-1), dict(min_chunk=-5),
+])
+def test_bad_config_rejected_without_gpu(T, kw):
+    base = dict(k=2048, max_rows=7, max_len=80_000)
+    base.update(kw)
+    cfg = T.make_config(**base)
+    with pytest.raises(T.TopKError) as e:
+        T.topk_query_sizes(cfg)
+    assert e.value.status == T.TOPK_ERR_INVALID_ARG
+
+
+def test_reserved_must_be_zero(T):
+    cfg = T.make_config(2048, 7, 80_000)
+    cfg.reserved[2] = 1
+    with pytest.raises(T.TopKError) as e:
+        T.topk_query_sizes(cfg)
+    assert e.value.status == T.TOPK_ERR_INVALID_ARG
+
+
+def test_register_path_too_long_is_unsupported(T):
+    cfg = T.make_config(2048, 2, 16385, force_path="register")
+    with pytest.raises(T.TopKError) as e:
+        T.topk_query_sizes(cfg)
+    assert e.value.status == T.TOPK_ERR_UNSUPPORTED
+
+
+def test_null_arguments_rejected(T):
+    lib = T.load_library()
+    cfg = T.make_config(2048, 7, 80_000)
+    assert lib.topk_query_sizes(ctypes.byref(cfg), None, None) == T.TOPK_ERR_INVALID_ARG
+    assert lib.topk_query_sizes(None, None, None) == T.TOPK_ERR_INVALID_ARG
+    assert lib.topk_workspace_init(None, 256, None) == T.TOPK_ERR_INVALID_ARG
+    v = ctypes.c_int32(0)
+    assert lib.topk_read_status(None, 256, ctypes.byref(v), None) == T.TOPK_ERR_INVALID_ARG
+    assert lib.topk_debug_keys(None, 5, None, None, None) == T.TOPK_ERR_INVALID_ARG
+    bad = T.make_config(0, 7, 80_000)
+    assert lib.topk_plan(ctypes.byref(bad), None, 7, None, 0, None) == T.TOPK_ERR_INVALID_ARG
+    assert lib.topk_select_paged(ctypes.byref(bad), None, None, 0, None, 7, None, 0, 64,
+                                 None, None, 2048, None, 0, None) == T.TOPK_ERR_INVALID_ARG
+
+
+def test_valid_config_needs_a_device(T):
+    """With no GPU in this container a valid configuration reaches the device
+    query and reports a HIP error rather than crashing."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(T.TopKError) as e:
+        T.topk_query_sizes(T.make_config(2048, 7, 80_000))
+    assert e.value.status == T.TOPK_ERR_HIP

@@ -1,0 +1,155 @@
+"""Parity of the HIP path with the CPU oracle (MI355X).
+
+Every comparison is bit-exact after canonical ordering by position: the set of
+selected positions, their slots, and the -1 padding. The five workloads run at
+full size under the planner's choice and under each forced path; seeded fuzz
+cases cover ragged and empty rows, heavy ties, +-0 and -inf, page sizes,
+shared and per-row tables, the candidate-overflow fallback, slot-only output
+and unaligned score rows.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import synth
+from tests import _gpu
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+
+@pytest.fixture(scope="module")
+def configs():
+    return {i: synth.make_config(i) for i in range(1, 6)}
+
+
+CONFIG_CASES = [
+    (1, "auto", {}), (1, "register", {}), (1, "single", {}), (1, "multi", {}), (1, "multi", {"wg_per_row": 4}),
+    (2, "auto", {}), (2, "single", {}), (2, "multi", {"wg_per_row": 8}), (2, "multi", {"wg_per_row": 36}),
+    (3, "auto", {}), (3, "single", {}), (3, "multi", {"cand_capacity": 64}),
+    (4, "auto", {}), (4, "single", {}), (4, "multi", {}),
+    (5, "auto", {}), (5, "single", {}), (5, "multi", {}), (5, "multi", {"cand_capacity": 512}),
+]
+
+
+@pytest.mark.parametrize("i,path,kw", CONFIG_CASES,
+                         ids=[f"c{i}-{p}-{'-'.join(f'{k}{v}' for k, v in kw.items())}" for i, p, kw in CONFIG_CASES])
+def test_config_parity(configs, i, path, kw):
+    w = configs[i]
+    _gpu.say(f"[parity] config {i} {w.name} path={path} {kw}")
+    got = _gpu.run_gpu(w, path, **kw)
+    _gpu.assert_matches_oracle(w, got, f"c{i} {path} {kw}")
+
+
+def test_config_invariants_independent_of_oracle(configs):
+    for i in (1, 2, 4):
+        w = configs[i]
+        got = _gpu.run_gpu(w, "auto")
+        _gpu.assert_invariants(w, got, label=f"c{i}")
+
+
+FUZZ = []
+for s in range(24):
+    FUZZ.append(dict(seed=100 + s, rows=1 + (s * 7) % 13, max_len=[300, 2100, 5000, 17000, 40000][s % 5],
+                     alphabet=[0, 3, 40, 0][s % 4], special=bool(s % 3 == 0), page_size=[64, 1, 16, 128, 48][s % 5],
+                     shared_table=bool(s % 2), stride_pad=[0, 3, 8][s % 3],
+                     path=["auto", "single", "multi", "auto"][s % 4]))
+
+
+@pytest.mark.parametrize("case", FUZZ, ids=[f"fuzz{c['seed']}" for c in FUZZ])
+def test_fuzz_parity(case):
+    c = dict(case)
+    path = c.pop("path")
+    seed = c.pop("seed")
+    w = synth.random_case(seed, **c)
+    if path == "register" and w.max_len > 16384:
+        path = "single"
+    _gpu.say(f"[fuzz] seed {seed} rows {w.rows} max_len {w.max_len} k {w.k} ps {w.page_size} path {path}")
+    got = _gpu.run_gpu(w, path, max_len=w.stride)
+    _gpu.assert_matches_oracle(w, got, f"fuzz {seed}")
+    _gpu.assert_invariants(w, got, label=f"fuzz {seed}")
+
+
+@pytest.mark.parametrize("k", [1, 2, 63, 64, 65, 1000, 2047, 2048])
+@pytest.mark.parametrize("path", ["auto", "multi"])
+def test_k_values(k, path):
+    w = synth.random_case(7 + k, rows=5, max_len=30000, alphabet=50, k=k, exact_len=True)
+    _gpu.say(f"[k] k {k} path {path}")
+    got = _gpu.run_gpu(w, path)
+    _gpu.assert_matches_oracle(w, got, f"k {k}")
+
+
+def test_register_path_exact_tile():
+    w = synth.random_case(5, rows=3, max_len=16384, alphabet=9, k=2048, exact_len=True)
+    _gpu.assert_matches_oracle(w, _gpu.run_gpu(w, "register"), "register 16384")
+
+
+@pytest.mark.parametrize("cap", [1, 8, 300])
+def test_candidate_overflow_fallback(cap):
+    w = synth.random_case(31, rows=4, max_len=60000, alphabet=5, k=1500, exact_len=True)
+    _gpu.say(f"[overflow] cap {cap}")
+    got = _gpu.run_gpu(w, "multi", cand_capacity=cap)
+    _gpu.assert_matches_oracle(w, got, f"cap {cap}")
+
+
+def test_slots_only_output(configs):
+    w = configs[2]
+    got = _gpu.run_gpu(w, "auto", with_idx=False)
+    _gpu.assert_matches_oracle(w, got, "slots only")
+
+
+def test_unaligned_scores():
+    w = synth.random_case(41, rows=6, max_len=25000, stride_pad=1, alphabet=30, k=900)
+    got = _gpu.run_gpu(w, "multi", scores_offset=1, max_len=w.stride)
+    _gpu.assert_matches_oracle(w, got, "unaligned")
+    got = _gpu.run_gpu(w, "single", scores_offset=1, max_len=w.stride)
+    _gpu.assert_matches_oracle(w, got, "unaligned single")
+
+
+def test_repeated_calls_reuse_plan_and_workspace(configs):
+    w = configs[3]
+    outs = _gpu.run_gpu(w, "auto", repeat=3)
+    for got in outs:
+        _gpu.assert_matches_oracle(w, got, "repeat")
+
+
+def test_empty_and_tiny_rows():
+    st = synth.Stream(77)
+    lengths = np.array([0, 1, 2, 2048, 2049, 0, 5000], np.int32)
+    stride = 5000
+    scores = synth._f32(st.normal(7 * stride)).reshape(7, stride)
+    bt = synth.page_permutation_tables(st, 7, (stride + 63) // 64)
+    w = synth.Workload("tiny", scores, lengths, bt, bt.shape[1], 64, 2048, 77)
+    for path in ("auto", "single", "multi"):
+        _gpu.assert_matches_oracle(w, _gpu.run_gpu(w, path), f"tiny {path}")
+
+
+def test_debug_keys_match_fp16_definition():
+    """Device bins equal the top 10 bits of the ordered key of numpy's FP16
+    rounding (RNE) of each score, with -0 folded into +0; device FP32 keys
+    order like the scores."""
+    from sparse_attention_indexer_amd import topk
+    st = synth.Stream(5)
+    x = np.concatenate([
+        synth._f32(st.normal(200_000) * np.exp(st.normal(200_000) * 4)),
+        np.array([0.0, -0.0, np.inf, -np.inf, 65504, 65520, -65520, 1e-8, -1e-8, 6e-8, 2.98e-8,
+                  np.finfo(np.float32).tiny, -np.finfo(np.float32).tiny, 1e-45, -1e-45], np.float32),
+        np.arange(65536, dtype=np.uint16).view(np.float16).astype(np.float32),
+    ]).astype(np.float32)
+    x = x[~np.isnan(x)]
+    bins, keys = topk.topk_debug_keys(torch.from_numpy(x).cuda())
+    bins = bins.cpu().numpy().view(np.uint32)
+    keys = keys.cpu().numpy().view(np.uint32)
+    h = x.astype(np.float16)
+    h[h == 0] = np.float16(0.0)
+    hb = h.view(np.uint16).astype(np.uint32)
+    key16 = np.where(hb & 0x8000, (~hb) & 0xFFFF, hb | 0x8000)
+    np.testing.assert_array_equal(bins, key16 >> 6)
+    order = np.argsort(x, kind="stable")
+    xs, ks = x[order], keys[order]
+    assert (np.diff(ks.astype(np.int64))[np.diff(xs) > 0] > 0).all()
+    assert (ks[1:][np.diff(xs) == 0] == ks[:-1][np.diff(xs) == 0]).all()
