@@ -80,6 +80,8 @@ topk_status sizing(const topk_config* cfg, Sizing* s) {
                                        : (cfg->max_len < kDefaultCandCap ? cfg->max_len : kDefaultCandCap);
   s->cand_cap = cap < 1 ? 1 : cap;
   const bool splits = cfg->force_path == TOPK_PATH_AUTO || cfg->force_path == TOPK_PATH_MULTI;
+  // every row split needs its own group state and at least two workgroups of one grid round
+  if (cfg->force_path == TOPK_PATH_MULTI && (int64_t)cfg->max_rows * 2 > s->grid) return TOPK_ERR_UNSUPPORTED;
   if (splits && cfg->wg_per_row > 0) {
     // a fixed group size must fit one grid round for every row at once
     if ((int64_t)cfg->wg_per_row * cfg->max_rows > s->grid || cfg->max_rows > s->max_groups)

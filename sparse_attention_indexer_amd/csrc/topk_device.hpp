@@ -40,21 +40,52 @@ __device__ __forceinline__ uint32_t first_lane(uint64_t m) {
   return (uint32_t)__builtin_ctzll(m);
 }
 
+// A value every lane holds equally (an LDS broadcast), moved to a scalar
+// register so that it costs no VGPR and branches on it stay uniform.
+__device__ __forceinline__ uint32_t uni(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+
 __device__ __forceinline__ uint32_t read_lane(uint32_t v, uint32_t l) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, (int)l);
 }
 
-__device__ __forceinline__ uint32_t wave_inclusive_add(uint32_t x) {
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t x) {
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, (unsigned)d, 64);
-    if (lane() >= (uint32_t)d) x += y;
+  for (int d = 32; d >= 1; d >>= 1) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, d, 64);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), d, 64);
+    x += ((uint64_t)hi << 32) | lo;
   }
   return x;
 }
 
-// Exclusive prefix sum over the workgroup in thread order. `scratch` holds
-// kWaves words of LDS. Every thread must call it.
+// Wave64 inclusive prefix sum with DPP lane moves: row_shr 1/2/4/8 scan each
+// 16-lane row, row_bcast 15/31 carry row totals forward (rows 1,3 then 2,3).
+// A few VALU operations instead of six LDS cross-lane round trips.
+#define SATOPK_DPP(x, ctrl, rmask) ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)(x), (ctrl), (rmask), 0xf, false))
+__device__ __forceinline__ uint32_t wave_inclusive_add(uint32_t x) {
+  x += SATOPK_DPP(x, 0x111, 0xf);  // row_shr:1
+  x += SATOPK_DPP(x, 0x112, 0xf);  // row_shr:2
+  x += SATOPK_DPP(x, 0x114, 0xf);  // row_shr:4
+  x += SATOPK_DPP(x, 0x118, 0xf);  // row_shr:8
+  x += SATOPK_DPP(x, 0x142, 0xa);  // row_bcast:15
+  x += SATOPK_DPP(x, 0x143, 0xc);  // row_bcast:31
+  return x;
+}
+
+// Maximum over the wave (every lane receives it).
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+  x = max(x, SATOPK_DPP(x, 0x111, 0xf));
+  x = max(x, SATOPK_DPP(x, 0x112, 0xf));
+  x = max(x, SATOPK_DPP(x, 0x114, 0xf));
+  x = max(x, SATOPK_DPP(x, 0x118, 0xf));
+  x = max(x, SATOPK_DPP(x, 0x142, 0xa));
+  x = max(x, SATOPK_DPP(x, 0x143, 0xc));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+// Exclusive prefix sum over a workgroup of NW waves, in thread order.
+// `scratch` holds NW words of LDS. Every thread must call it.
+template <int NW = kWaves>
 __device__ __forceinline__ uint32_t block_exclusive_add(uint32_t x, uint32_t* scratch,
                                                         uint32_t* total = nullptr) {
   const uint32_t w = threadIdx.x >> 6;
@@ -63,7 +94,7 @@ __device__ __forceinline__ uint32_t block_exclusive_add(uint32_t x, uint32_t* sc
   __syncthreads();
   uint32_t pre = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
+  for (int i = 0; i < NW; ++i) {
     const uint32_t s = scratch[i];
     pre += ((uint32_t)i < w) ? s : 0u;
     tot += s;
@@ -92,28 +123,36 @@ __device__ __forceinline__ void hist_add(uint32_t* h, bool m, uint32_t bin) {
 // Scan `nb` bins from the top and find the bin holding the need-th largest
 // element: above(b) < need <= above(b) + h[b]. Writes (b, above(b), h[b]) to
 // result[0..2]. PB bins per thread; nb <= PB * kBlock; 1 <= need <= sum(h).
-template <int PB>
+// Bin b lives at hist[b + (b >> PAD)] when PAD > 0: one pad word per 2^PAD
+// bins keeps the lanes' contiguous PB-bin reads on distinct LDS banks.
+template <int PB, int PAD = 0>
+__device__ __forceinline__ uint32_t bin_addr(int b) { return PAD ? (uint32_t)(b + (b >> PAD)) : (uint32_t)b; }
+
+template <int PB, int PAD = 0>
 __device__ __forceinline__ void find_threshold(const uint32_t* hist, int nb, uint32_t need,
                                                uint32_t* scratch, uint32_t* result) {
   const int t = threadIdx.x;
-  uint32_t h[PB];
   uint32_t s = 0;
 #pragma unroll
   for (int j = 0; j < PB; ++j) {
     const int b = nb - 1 - (t * PB + j);
-    h[j] = b >= 0 ? hist[b] : 0u;
-    s += h[j];
+    s += b >= 0 ? hist[bin_addr<PB, PAD>(b)] : 0u;
   }
   uint32_t cum = block_exclusive_add(s, scratch);
-#pragma unroll
-  for (int j = 0; j < PB; ++j) {
-    const int b = nb - 1 - (t * PB + j);
-    if (cum < need && need <= cum + h[j]) {
-      result[0] = (uint32_t)b;
-      result[1] = cum;
-      result[2] = h[j];
+  // Only the thread whose bins straddle `need` re-reads them (cheap LDS reads
+  // instead of PB registers held across the scan).
+  if (cum < need && need <= cum + s) {
+    for (int j = 0; j < PB; ++j) {
+      const int b = nb - 1 - (t * PB + j);
+      const uint32_t h = b >= 0 ? hist[bin_addr<PB, PAD>(b)] : 0u;
+      if (cum < need && need <= cum + h) {
+        result[0] = (uint32_t)b;
+        result[1] = cum;
+        result[2] = h;
+        break;
+      }
+      cum += h;
     }
-    cum += h[j];
   }
   __syncthreads();
 }

@@ -30,19 +30,37 @@ namespace satopk {
 // ---------------------------------------------------------------------------
 // Planning kernel: one workgroup reads the device lengths and writes the plan.
 // ---------------------------------------------------------------------------
-constexpr int kPlanBlock = 1024;
+constexpr int kPlanBlock = 256;
 
 __device__ __forceinline__ int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __device__ __forceinline__ int64_t round_up64(int64_t a, int64_t b) { return ceil_div64(a, b) * b; }
 
-// Workgroups a row gets for target chunk `chunk`; 1 = the row stays whole.
-// `chunk_out` receives the aligned chunk length actually used.
-__device__ __forceinline__ int split_of(int32_t len, int32_t k, int64_t chunk, bool force_split,
-                                        int32_t fixed_g, int64_t* chunk_out) {
+// Workgroups a row of `len` scores gets (1 = the row stays whole).
+//  - fixed: a fixed group size for every row longer than k;
+//  - force_split: at least 2, the grid's remaining workgroups shared in
+//    proportion to length (at most 2 per row + the rest: fits one round);
+//  - otherwise: the grid shared in proportion to length, floor-rounded so the
+//    split rows' workgroups fit one round of the persistent grid, and no
+//    chunk shorter than min_chunk.
+// The chunk is then aligned to kChunkAlign, which can only lower the count.
+__device__ __forceinline__ int split_of(int32_t len, const PlanArgs& a, uint64_t total, int32_t n_long,
+                                        int64_t* chunk_out) {
   *chunk_out = len;
-  if (len <= k) return 1;
-  int64_t g = fixed_g > 0 ? fixed_g : ceil_div64(len, chunk);
-  if (force_split && g < 2) g = 2;
+  if (len <= a.k || total == 0) return 1;
+  int64_t g;
+  if (a.wg_per_row > 0) {
+    g = a.wg_per_row;
+  } else if (a.force_path == TOPK_PATH_MULTI) {
+    const int64_t spare = (int64_t)a.grid - 2 * (int64_t)n_long;
+    g = 2 + (spare > 0 ? (int64_t)((uint64_t)spare * (uint64_t)len / total) : 0);
+  } else if (a.force_path == TOPK_PATH_REGISTER || a.force_path == TOPK_PATH_SINGLE) {
+    return 1;
+  } else {
+    g = (int64_t)((uint64_t)a.grid * (uint64_t)len / total);
+    const int64_t min_chunk = a.min_chunk > 0 ? a.min_chunk : kDefaultMinChunk;
+    const int64_t by_min = len / min_chunk;
+    if (g > by_min) g = by_min;
+  }
   if (g < 2) return 1;
   const int64_t c = round_up64(ceil_div64(len, g), kChunkAlign);
   g = ceil_div64(len, c);
@@ -51,66 +69,65 @@ __device__ __forceinline__ int split_of(int32_t len, int32_t k, int64_t chunk, b
   return (int)g;
 }
 
+constexpr int kPlanWaves = kPlanBlock / 64;
+
 __global__ void __launch_bounds__(kPlanBlock) topk_plan_kernel(PlanArgs a) {
-  __shared__ unsigned long long s_total;
-  __shared__ int s_items, s_groups, s_ok;
-  __shared__ uint32_t s_scan[kPlanBlock / 64];
+  __shared__ uint64_t s_red[kPlanWaves];
+  __shared__ uint32_t s_scan[kPlanWaves];
   __shared__ int s_carry_multi, s_carry_groups, s_carry_single;
   const int t = threadIdx.x;
-  const bool no_split = a.force_path == TOPK_PATH_REGISTER || a.force_path == TOPK_PATH_SINGLE;
-  const bool force_split = a.force_path == TOPK_PATH_MULTI;
 
-  if (t == 0) s_total = 0;
-  __syncthreads();
-  unsigned long long mine = 0;
+  // Total length and count of the rows longer than k (wave sums, then one
+  // LDS word per wave: no same-address atomics).
+  uint64_t mine = 0;
+  uint32_t longs = 0;
   for (int r = t; r < a.num_rows; r += kPlanBlock) {
     const int32_t len = a.lengths[r];
-    if (len > a.k) mine += (unsigned long long)len;
-  }
-  atomicAdd(&s_total, mine);
-  __syncthreads();
-
-  // Target chunk: spread the batch's work over the persistent grid, then grow
-  // the chunk until the split rows' items fit in one round of the grid.
-  int64_t chunk = round_up64((int64_t)a.min_chunk > 0 ? a.min_chunk : kDefaultMinChunk, kChunkAlign);
-  const int64_t even = round_up64(ceil_div64((int64_t)s_total, a.grid > 0 ? a.grid : 1), kChunkAlign);
-  if (even > chunk) chunk = even;
-  if (no_split) chunk = (int64_t)1 << 40;
-  for (int iter = 0; iter < 128; ++iter) {
-    if (t == 0) { s_items = 0; s_groups = 0; }
-    __syncthreads();
-    int items = 0, groups = 0;
-    for (int r = t; r < a.num_rows; r += kPlanBlock) {
-      int64_t c;
-      const int g = split_of(a.lengths[r], a.k, chunk, force_split, a.wg_per_row, &c);
-      if (g > 1) { items += g; groups += 1; }
+    if (len > a.k) {
+      mine += (uint64_t)len;
+      ++longs;
     }
-    atomicAdd(&s_items, items);
-    atomicAdd(&s_groups, groups);
-    __syncthreads();
-    const bool fits = s_items <= a.grid && s_groups <= a.max_groups;
-    __syncthreads();
-    if (fits || a.wg_per_row > 0) break;
-    chunk = round_up64(chunk + chunk / 4 + kChunkAlign, kChunkAlign);
   }
-  const int total_multi = s_items;
+  mine = wave_sum_u64(mine + ((uint64_t)longs << 40));   // lengths < 2^31, rows < 2^23
+  if (lane() == 0) s_red[t >> 6] = mine;
+  __syncthreads();
+  uint64_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < kPlanWaves; ++i) packed += s_red[i];
+  const uint64_t total = packed & ((1ull << 40) - 1);
+  const int32_t n_long = (int32_t)(packed >> 40);
   if (t == 0) {
-    s_ok = (s_items <= a.grid && s_groups <= a.max_groups) ? 1 : 0;
     s_carry_multi = 0;
     s_carry_groups = 0;
     s_carry_single = 0;
   }
   __syncthreads();
-  if (!s_ok) {  // only reachable with a fixed wg_per_row the host let through
+
+  // Items: split rows first (indices [0, total_multi), one grid round), then
+  // one item per whole row. Three scans over each block of rows.
+  // First count the split rows' items so whole rows can start after them.
+  uint32_t my_multi = 0, my_groups = 0;
+  for (int r = t; r < a.num_rows; r += kPlanBlock) {
+    int64_t c;
+    const int g = split_of(a.lengths[r], a, total, n_long, &c);
+    if (g > 1) {
+      my_multi += (uint32_t)g;
+      my_groups += 1;
+    }
+  }
+  uint32_t total_multi_u, total_groups_u;
+  block_exclusive_add<kPlanWaves>(my_multi, s_scan, &total_multi_u);
+  block_exclusive_add<kPlanWaves>(my_groups, s_scan, &total_groups_u);
+  const int total_multi = (int)total_multi_u;
+  if (total_multi > a.grid || (int)total_groups_u > a.max_groups) {
+    // unreachable for configurations the host accepts; never hand out a
+    // plan whose split rows cannot all be resident at once
     if (t == 0) {
       a.header->magic = 0;
       a.header->num_items = 0;
     }
     return;
   }
-
-  // Items: split rows first (indices [0, total_multi), one grid round), then
-  // one item per whole row.
   for (int r0 = 0; r0 < a.num_rows; r0 += kPlanBlock) {
     const int r = r0 + t;
     int g = 0;
@@ -118,16 +135,15 @@ __global__ void __launch_bounds__(kPlanBlock) topk_plan_kernel(PlanArgs a) {
     int32_t len = 0;
     if (r < a.num_rows) {
       len = a.lengths[r];
-      g = split_of(len, a.k, chunk, force_split, a.wg_per_row, &c);
+      g = split_of(len, a, total, n_long, &c);
     }
     const uint32_t n_multi = (r < a.num_rows && g > 1) ? (uint32_t)g : 0u;
     const uint32_t n_group = n_multi ? 1u : 0u;
     const uint32_t n_single = (r < a.num_rows && g == 1) ? 1u : 0u;
-    // three scans packed: multi items in 16 bits would overflow, so run them apart
     uint32_t tot_m, tot_g, tot_s;
-    const uint32_t off_m = block_exclusive_add(n_multi, s_scan, &tot_m);
-    const uint32_t off_g = block_exclusive_add(n_group, s_scan, &tot_g);
-    const uint32_t off_s = block_exclusive_add(n_single, s_scan, &tot_s);
+    const uint32_t off_m = block_exclusive_add<kPlanWaves>(n_multi, s_scan, &tot_m);
+    const uint32_t off_g = block_exclusive_add<kPlanWaves>(n_group, s_scan, &tot_g);
+    const uint32_t off_s = block_exclusive_add<kPlanWaves>(n_single, s_scan, &tot_s);
     const int base_m = s_carry_multi, base_g = s_carry_groups, base_s = s_carry_single;
     if (n_multi) {
       const int first = base_m + (int)off_m;
@@ -140,7 +156,8 @@ __global__ void __launch_bounds__(kPlanBlock) topk_plan_kernel(PlanArgs a) {
         w.end = (int32_t)(e < len ? e : len);
         w.group = gid;
         w.gsize = g;
-        w.pad[0] = w.pad[1] = w.pad[2] = 0;
+        w.len = len;
+        w.pad[0] = w.pad[1] = 0;
         a.items[first + j] = w;
       }
     }
@@ -151,7 +168,8 @@ __global__ void __launch_bounds__(kPlanBlock) topk_plan_kernel(PlanArgs a) {
       w.end = len;
       w.group = -1;
       w.gsize = 1;
-      w.pad[0] = w.pad[1] = w.pad[2] = 0;
+      w.len = (len < 0 || (int64_t)len > a.max_len) ? -1 : len;
+      w.pad[0] = w.pad[1] = 0;
       a.items[total_multi + base_s + (int)off_s] = w;
     }
     __syncthreads();
@@ -171,7 +189,8 @@ __global__ void __launch_bounds__(kPlanBlock) topk_plan_kernel(PlanArgs a) {
     h.grid = a.grid;
     h.k = a.k;
     h.num_groups = s_carry_groups;
-    h.chunk = (int32_t)(chunk > 0x7FFFFFFF ? 0x7FFFFFFF : chunk);
+    const uint64_t even = total / (uint64_t)(a.grid > 0 ? a.grid : 1);
+    h.chunk = (int32_t)(even > 0x7FFFFFFFull ? 0x7FFFFFFFull : even);
     for (int i = 0; i < 8; ++i) h.pad[i] = 0;
     *a.header = h;
   }
@@ -211,7 +230,8 @@ constexpr uint32_t kFirstBin = 15, kLastBin = 1008;   // -inf bin, +inf bin
 constexpr uint32_t kNotFound = 0xFFFFFFFFu;
 
 // For threshold bin b*: bin(x) >= b* <=> h >= vlo and bin(x) > b* <=> h >= vhi,
-// with h the canonical FP16 of x (FP16 order agrees with key order off -0/NaN).
+// with h the canonical FP16 of x (FP16 order agrees with key order off -0/NaN;
+// FP16 denormals are kept, so the comparison is exact).
 struct Cut {
   _Float16 vlo, vhi;
 };
@@ -226,10 +246,36 @@ __device__ __forceinline__ Cut cut_of_bin(uint32_t b) {
   return c;
 }
 
+// Cross-workgroup traffic goes through device-coherent operations only:
+// atomics, and loads/stores at agent scope (which bypass the non-coherent
+// per-XCD L2). Each wave drains its own memory operations before the
+// workgroup barrier that precedes an arrival count, so no whole-cache
+// writeback or invalidate (an agent-scope fence) is ever needed.
+__device__ __forceinline__ void drain_memory() { __builtin_amdgcn_s_waitcnt(0); }
+template <class T>
+__device__ __forceinline__ T ld_agent(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ void st_agent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr int kFirstRadixBits = 13;                 // first refinement digit (histogram in the list region)
+constexpr int kFirstRadixBins = 1 << kFirstRadixBits;
+constexpr int kWidePad = 4;                         // one pad word per 16 bins: conflict-free threshold scan
+constexpr int kWideWords = kFirstRadixBins + (kFirstRadixBins >> kWidePad);
+constexpr int kWideSlots = kWideWords / 2;          // list entries the padded histogram occupies
+constexpr int kLoadBatch = 24;                      // candidates per lane in flight when the resolver fills LDS
+constexpr int kResolveRegs = 24;                    // candidates per lane of the register-resident first pass
+static_assert(kWideWords * 4 <= kListCap * 8, "first-digit histogram aliases the LDS list");
+static_assert(kMaxK <= kRadixBins, "above-threshold staging aliases rhist");
+
 struct __align__(16) Smem {
-  uint64_t list[kListCap];      // boundary candidates (key32 << 32 | position)
+  uint64_t list[kListCap];      // boundary candidates: (key32 << 32 | position), then composite keys
   uint32_t lhist[kBins];        // this workgroup's histogram (raw index)
-  uint32_t rhist[kRadixBins];   // refinement digits; also the merged histogram
+  uint32_t rhist[kRadixBins];   // refinement digits; merged histogram; staged above-threshold positions
+  uint32_t outpos[kMaxK];       // a row's selected positions, by output index, until the flush
   uint32_t scratch[kWaves];
   uint32_t res[4];
   uint32_t cur_out;             // next output position of the row
@@ -241,6 +287,10 @@ struct __align__(16) Smem {
 
 // Output of one row: slot = table[i / ps] * ps + i % ps (page: TopK-V2,
 // selected logical positions translated to physical indexer KV-cache slots).
+// write() stages a position in LDS; flush() then maps and stores a range of
+// outputs with all block-table loads in flight at once. Every write checks
+// its bounds and returns false instead of writing out of range; callers
+// gather the flags and report them once (report_bad).
 struct RowOut {
   int32_t* slots;
   int32_t* idx;
@@ -248,35 +298,58 @@ struct RowOut {
   int32_t ps;
   int32_t shift;
   uint32_t k;
+  uint32_t len;      // valid positions of the row
   int32_t* status;
+  uint32_t* stage;   // LDS, k entries
 
-  __device__ __forceinline__ void write(uint32_t pos, int32_t i) const {
-    if (pos >= k) {  // counts and classification disagree: never write past the row
-      atomicOr(status, TOPK_DEVICE_INTERNAL);
-      return;
+  __device__ __forceinline__ bool write(uint32_t pos, int32_t i) const {
+    const bool ok = pos < k;
+    if (ok) stage[pos] = (uint32_t)i;
+    return ok;
+  }
+
+  __device__ __forceinline__ int32_t page(int32_t i) const {
+    return shift >= 0 ? table[i >> shift] : table[i / ps];
+  }
+
+  // Output pos <- position i whose block-table entry `pg` is already known.
+  __device__ __forceinline__ bool store_page(uint32_t pos, int32_t i, int32_t pg) const {
+    const bool ok = pos < k && (uint32_t)i < len;
+    if (ok) {
+      slots[pos] = pg * ps + (shift >= 0 ? (i & (ps - 1)) : (i % ps));
+      if (idx) idx[pos] = i;
     }
-    int32_t page, off;
-    if (shift >= 0) {
-      page = table[i >> shift];
-      off = i & (ps - 1);
-    } else {
-      page = table[i / ps];
-      off = i % ps;
-    }
-    slots[pos] = page * ps + off;
-    if (idx) idx[pos] = i;
+    return ok;
+  }
+
+  __device__ __forceinline__ bool store(uint32_t pos, int32_t i) const {
+    const bool ok = pos < k && (uint32_t)i < len;   // never index the table past the row
+    return ok ? store_page(pos, i, page(i)) : false;
+  }
+
+  // Whole workgroup; staged outputs [from, to).
+  __device__ __forceinline__ bool flush(uint32_t from, uint32_t to) const {
+    bool ok = true;
+    for (uint32_t j = from + threadIdx.x; j < to; j += kBlock) ok &= store(j, (int32_t)stage[j]);
+    return ok;
   }
 };
 
+// One device-status flag for every lane that saw an inconsistency (counts and
+// classification disagreeing, which valid inputs never cause). Whole wave.
+__device__ __forceinline__ void report_bad(bool bad, int32_t* status) {
+  if (__ballot(bad) != 0ull && lane() == 0) atomicOr(status, TOPK_DEVICE_INTERNAL);
+}
+
 // Wave-aggregated output: one LDS atomic per wave reserves positions.
-__device__ __forceinline__ void emit_wave(bool take, int32_t i, uint32_t* cursor, const RowOut& o) {
+__device__ __forceinline__ bool emit_wave(bool take, int32_t i, uint32_t* cursor, const RowOut& o) {
   const uint64_t m = __ballot(take);
-  if (m == 0) return;
+  if (m == 0) return true;
   const uint32_t leader = first_lane(m);
   uint32_t base = 0;
   if (lane() == leader) base = atomicAdd(cursor, (uint32_t)__popcll(m));
   base = read_lane(base, leader);
-  if (take) o.write(base + mbcnt(m), i);
+  return take ? o.write(base + mbcnt(m), i) : true;
 }
 
 __device__ __forceinline__ void push_wave(bool take, uint64_t v, uint32_t* cursor, uint64_t* dst) {
@@ -287,12 +360,6 @@ __device__ __forceinline__ void push_wave(bool take, uint64_t v, uint32_t* curso
   if (lane() == leader) base = atomicAdd(cursor, (uint32_t)__popcll(m));
   base = read_lane(base, leader);
   if (take) dst[base + mbcnt(m)] = v;
-}
-
-__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) x = max(x, (uint32_t)__shfl_xor(x, d, 64));
-  return x;
 }
 
 // Element j = q * 4 + c of a lane's tile sits at this position: lane t loads
@@ -354,44 +421,64 @@ __device__ __forceinline__ void hist_packed(const uint32_t (&hk)[kHk], uint32_t*
 }
 
 // Bit j set <=> element j lies in the threshold bin or above it.
-__device__ __forceinline__ uint32_t interest_mask(const uint32_t (&hk)[kHk], _Float16 vlo) {
-  uint32_t m = 0;
+__device__ __forceinline__ uint64_t interest_mask(const uint32_t (&hk)[kHk], _Float16 vlo) {
+  uint32_t lo = 0, hi = 0;
 #pragma unroll
-  for (int i = 0; i < kHk; ++i) {
-    m |= (uint32_t)(half_lo(hk[i]) >= vlo) << (2 * i);
-    m |= (uint32_t)(half_hi(hk[i]) >= vlo) << (2 * i + 1);
+  for (int i = 0; i < kHk / 2; ++i) {
+    lo |= (uint32_t)(half_lo(hk[i]) >= vlo) << (2 * i);
+    lo |= (uint32_t)(half_hi(hk[i]) >= vlo) << (2 * i + 1);
+    hi |= (uint32_t)(half_lo(hk[i + kHk / 2]) >= vlo) << (2 * i);
+    hi |= (uint32_t)(half_hi(hk[i + kHk / 2]) >= vlo) << (2 * i + 1);
   }
-  return m;
+  return ((uint64_t)hi << 32) | lo;
 }
+static_assert(kEpt == 64, "interest_mask packs one bit per tile element into 64 bits");
 
 // Per-lane running range of the boundary candidates, all kept as maxima.
 struct Range {
   uint32_t kmax = 0, kmin_inv = 0, imax = 0, imin_inv = 0;
 };
 
+// Re-reads go out kReload at a time so their latencies overlap. With a table,
+// each position's block-table entry is fetched in the same round trip and
+// handed to on_above, so staged outputs need no second lookup.
+constexpr int kReload = 4;
+
 // The few positions of `mask` are re-read as FP32 and classified: above the
-// threshold bin -> written to the output; in it -> counted into the range and
-// (when cand_dst is set) appended to the candidate list.
-__device__ __forceinline__ void extract(uint32_t mask, int32_t base, const float* rowp, _Float16 vhi,
-                                        uint32_t* cur_out, const RowOut& o, uint32_t* cur_cand,
-                                        uint64_t* cand_dst, uint32_t cand_limit, Range& rg) {
+// threshold bin -> on_above(position); in it -> counted into the range and
+// passed to on_cand(key32, position).
+template <class A, class C>
+__device__ __forceinline__ void extract(uint64_t mask, int32_t base, const float* rowp, _Float16 vhi, Range& rg,
+                                        A&& on_above, C&& on_cand, const RowOut* pages = nullptr) {
   while (mask) {
-    const int j = __builtin_ctz(mask);
-    mask &= mask - 1u;
-    const int32_t e = tile_pos(base, j >> 2, j & 3);
-    const float x = rowp[e];
-    if (half_lo(to_half2(x, x)) >= vhi) {
-      o.write(atomicAdd(cur_out, 1u), e);
-    } else {
-      const uint32_t kk = key32_of(x);
-      rg.kmax = max(rg.kmax, kk);
-      rg.kmin_inv = max(rg.kmin_inv, ~kk);
-      rg.imax = max(rg.imax, (uint32_t)e);
-      rg.imin_inv = max(rg.imin_inv, ~(uint32_t)e);
-      if (cand_dst) {
-        const uint32_t c = atomicAdd(cur_cand, 1u);
-        if (c < cand_limit) cand_dst[c] = ((uint64_t)kk << 32) | (uint32_t)e;
-        else atomicOr(o.status, TOPK_DEVICE_INTERNAL);
+    int32_t e[kReload];
+    bool v[kReload];
+#pragma unroll
+    for (int u = 0; u < kReload; ++u) {
+      v[u] = mask != 0ull;
+      const int j = v[u] ? __builtin_ctzll(mask) : 0;
+      mask &= mask - 1ull;
+      e[u] = tile_pos(base, j >> 2, j & 3);
+    }
+    float x[kReload];
+    int32_t pg[kReload];
+#pragma unroll
+    for (int u = 0; u < kReload; ++u) {
+      x[u] = v[u] ? rowp[e[u]] : 0.f;
+      pg[u] = (v[u] && pages) ? pages->page(e[u]) : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kReload; ++u) {
+      if (!v[u]) continue;
+      if (half_lo(to_half2(x[u], x[u])) >= vhi) {
+        on_above(e[u], pg[u]);
+      } else {
+        const uint32_t kk = key32_of(x[u]);
+        rg.kmax = max(rg.kmax, kk);
+        rg.kmin_inv = max(rg.kmin_inv, ~kk);
+        rg.imax = max(rg.imax, (uint32_t)e[u]);
+        rg.imin_inv = max(rg.imin_inv, ~(uint32_t)e[u]);
+        on_cand(kk, e[u]);
       }
     }
   }
@@ -417,34 +504,69 @@ __device__ __forceinline__ void find_threshold_raw(const uint32_t* hist, uint32_
                                                    uint32_t* result) {
   constexpr int PB = kBins / kBlock;
   const int t = threadIdx.x;
-  uint32_t h[PB];
   uint32_t s = 0;
 #pragma unroll
   for (int j = 0; j < PB; ++j) {
     const uint32_t b = (uint32_t)(kBins - 1 - (t * PB + j));
-    h[j] = (b >= kFirstBin && b <= kLastBin) ? hist[raw_of_bin(b)] : 0u;
-    s += h[j];
+    s += (b >= kFirstBin && b <= kLastBin) ? hist[raw_of_bin(b)] : 0u;
   }
   uint32_t cum = block_exclusive_add(s, scratch);
-#pragma unroll
-  for (int j = 0; j < PB; ++j) {
-    const uint32_t b = (uint32_t)(kBins - 1 - (t * PB + j));
-    if (cum < need && need <= cum + h[j]) {
-      result[0] = b;
-      result[1] = cum;
-      result[2] = h[j];
+  if (cum < need && need <= cum + s) {
+    for (int j = 0; j < PB; ++j) {
+      const uint32_t b = (uint32_t)(kBins - 1 - (t * PB + j));
+      const uint32_t h = (b >= kFirstBin && b <= kLastBin) ? hist[raw_of_bin(b)] : 0u;
+      if (cum < need && need <= cum + h) {
+        result[0] = b;
+        result[1] = cum;
+        result[2] = h;
+        break;
+      }
+      cum += h;
     }
-    cum += h[j];
   }
   __syncthreads();
 }
 
-// --- candidate sources for the exact refinement -----------------------------
-// each(f) calls f(valid, key32, position) for every element slot; the trip
-// count is uniform across the workgroup so wave-level ballots stay convergent.
+// Compressed composite key of a boundary candidate: the FP32 key offset from
+// the smallest candidate key, then the position reversed so that lower
+// positions rank higher. Distinct for distinct positions, so the top `need`
+// keys are unique, and the position is recoverable from the low b2 bits.
+struct Refine {
+  uint32_t lo32;
+  uint32_t b2;      // bits of the reversed position
+  uint32_t idx_hi;  // largest candidate position
+  uint32_t nb;      // total key bits
+  uint32_t need;    // boundary elements still to select
+  uint32_t cnt;     // boundary elements in total
+  __device__ __forceinline__ uint64_t key(uint32_t k32, int32_t i) const {
+    return ((uint64_t)(k32 - lo32) << b2) | (uint64_t)(idx_hi - (uint32_t)i);
+  }
+  __device__ __forceinline__ int32_t pos(uint64_t ck) const {
+    return (int32_t)(idx_hi - (uint32_t)(ck & ((1ull << b2) - 1ull)));
+  }
+};
 
-// A packed (key32 << 32 | position) list in LDS or global memory.
-struct ListSrc {
+__device__ __forceinline__ uint32_t bit_width(uint32_t x) { return x ? 32u - (uint32_t)__clz(x) : 0u; }
+
+// From the candidate range (kmax, ~kmin, imax, ~imin).
+__device__ __forceinline__ Refine make_refine(const uint32_t* range, uint32_t need, uint32_t cnt) {
+  Refine p;
+  const uint32_t kmax = uni(range[0]), kmin = ~uni(range[1]), imax = uni(range[2]), imin = ~uni(range[3]);
+  p.lo32 = kmin;
+  p.idx_hi = imax;
+  p.b2 = bit_width(imax - imin);
+  p.nb = bit_width(kmax - kmin) + p.b2;
+  p.need = need;
+  p.cnt = cnt;
+  return p;
+}
+
+// --- candidate sources for the exact refinement -----------------------------
+// each(f) calls f(valid, composite key) for every element slot; the trip count
+// is uniform across the workgroup so wave-level ballots stay convergent.
+
+// Composite keys already in LDS.
+struct KeyListSrc {
   const uint64_t* p;
   uint32_t n;
   template <class F>
@@ -452,8 +574,24 @@ struct ListSrc {
     for (uint32_t i0 = 0; i0 < n; i0 += kBlock) {
       const uint32_t i = i0 + threadIdx.x;
       const bool valid = i < n;
-      const uint64_t e = valid ? p[i] : 0ull;
-      f(valid, (uint32_t)(e >> 32), (int32_t)(uint32_t)e);
+      f(valid, valid ? p[i] : 0ull);
+    }
+  }
+};
+
+// (key32 << 32 | position) pairs that other workgroups left in global memory,
+// read with device-coherent loads.
+struct PairListSrc {
+  const uint64_t* p;
+  uint32_t n;
+  Refine r;
+  template <class F>
+  __device__ __forceinline__ void each(F&& f) const {
+    for (uint32_t i0 = 0; i0 < n; i0 += kBlock) {
+      const uint32_t i = i0 + threadIdx.x;
+      const bool valid = i < n;
+      const uint64_t e = valid ? ld_agent(p + i) : 0ull;
+      f(valid, r.key((uint32_t)(e >> 32), (int32_t)(uint32_t)e));
     }
   }
 };
@@ -464,6 +602,7 @@ struct StreamSrc {
   const float* rowp;
   int32_t begin, end;
   Cut cut;
+  Refine r;
   template <class F>
   __device__ __forceinline__ void each(F&& f) const {
     for (int32_t base = begin; base < end; base += 2 * kBlock * 4) {
@@ -493,94 +632,101 @@ struct StreamSrc {
         for (int c = 0; c < 4; ++c) {
           const int32_t e = base + (u * kBlock + (int)threadIdx.x) * 4 + c;
           const _Float16 h = half_lo(to_half2(x[u * 4 + c], 0.f));
-          f(e < end && h >= cut.vlo && !(h >= cut.vhi), key32_of(x[u * 4 + c]), e);
+          const bool in_bin = e < end && h >= cut.vlo && !(h >= cut.vhi);
+          f(in_bin, in_bin ? r.key(key32_of(x[u * 4 + c]), e) : 0ull);
         }
     }
   }
 };
 
-// Compressed composite key of a boundary candidate: the FP32 key offset from
-// the smallest candidate key, then the position reversed so that lower
-// positions rank higher. Distinct for distinct positions, so the top `need`
-// keys are unique.
-struct Refine {
-  uint32_t lo32;
-  uint32_t b2;      // bits of the reversed position
-  uint32_t idx_hi;  // largest candidate position
-  uint32_t nb;      // total key bits
-  uint32_t need;    // boundary elements still to select
-  uint32_t cnt;     // boundary elements in total
-  __device__ __forceinline__ uint64_t key(uint32_t k32, int32_t i) const {
-    return ((uint64_t)(k32 - lo32) << b2) | (uint64_t)(idx_hi - (uint32_t)i);
-  }
-};
-
-__device__ __forceinline__ uint32_t bit_width(uint32_t x) { return x ? 32u - (uint32_t)__clz(x) : 0u; }
-
-// From the candidate range (kmax, ~kmin, imax, ~imin).
-__device__ __forceinline__ Refine make_refine(const uint32_t* range, uint32_t need, uint32_t cnt) {
-  Refine p;
-  const uint32_t kmax = range[0], kmin = ~range[1], imax = range[2], imin = ~range[3];
-  p.lo32 = kmin;
-  p.idx_hi = imax;
-  p.b2 = bit_width(imax - imin);
-  p.nb = bit_width(kmax - kmin) + p.b2;
-  p.need = need;
-  p.cnt = cnt;
-  return p;
-}
-
 // Exact selection of the `need` best boundary candidates (FP32 value
-// descending, position ascending): MSB-first radix over kRadixBits-bit digits
-// of the composite key. Each pass histograms the digit of the candidates that
-// match the prefix fixed so far, finds the digit holding the need-th, emits
-// the candidates with a larger digit and keeps the equal ones; survivors are
-// compacted into LDS as soon as they fit. Outputs go to sh.cur_out onwards.
-// SRC_IN_LDS: the source is sh.list itself (no compaction into it).
+// descending, position ascending): MSB-first radix over the composite key.
+// Each pass histograms one digit of the candidates that match the prefix
+// fixed so far, finds the digit holding the need-th, emits the candidates
+// with a larger digit and keeps the equal ones; survivors are compacted into
+// free LDS list space as soon as they fit. The first pass takes a 13-bit
+// digit when 34 KB of the list are free for its (padded) histogram.
+// Outputs are staged from sh.cur_out onwards. SRC_IN_LDS: the source is the
+// composite-key list sh.list[0, n0). The search may resume after `pbits0`
+// key bits already fixed to `prefix0`, with `need0` still to select.
 template <bool SRC_IN_LDS, class Src>
-__device__ __forceinline__ void refine(const Src& src, const Refine& p, Smem& sh, const RowOut& o) {
+__device__ __forceinline__ void refine(const Src& src, const Refine& p, Smem& sh, const RowOut& o,
+                                       uint64_t prefix0, uint32_t pbits0, uint32_t need0, uint32_t n0) {
   const int t = threadIdx.x;
-  if (p.need == p.cnt) {
-    src.each([&](bool valid, uint32_t, int32_t i) { emit_wave(valid, i, &sh.cur_out, o); });
+  bool bad = false;
+  if (need0 == n0) {
+    src.each([&](bool valid, uint64_t ck) {
+      bad |= !emit_wave(valid && (ck >> (p.nb - pbits0)) == prefix0, p.pos(ck), &sh.cur_out, o);
+    });
+    report_bad(bad, o.status);
     __syncthreads();
     return;
   }
-  uint64_t prefix = 0;
-  uint32_t pbits = 0, need = p.need, list_n = 0;
-  bool in_list = false;
+  uint64_t prefix = prefix0;
+  uint32_t pbits = pbits0, need = need0;
+  bool in_list = SRC_IN_LDS;
+  uint32_t list_off = 0, list_n = SRC_IN_LDS ? n0 : 0u;   // current list: sh.list[list_off, +list_n)
   for (;;) {
-    const uint32_t width = min((uint32_t)kRadixBits, p.nb - pbits);
+    uint32_t* hist = sh.rhist;
+    bool wide = false;
+    if (pbits == 0) {
+      if (!in_list) {
+        hist = reinterpret_cast<uint32_t*>(sh.list);
+        wide = true;
+      } else if (list_off + list_n + kWideSlots <= (uint32_t)kListCap) {
+        hist = reinterpret_cast<uint32_t*>(sh.list + list_off + list_n);
+        wide = true;
+      }
+    }
+    const uint32_t width = min(wide ? (uint32_t)kFirstRadixBits : (uint32_t)kRadixBits, p.nb - pbits);
     const uint32_t shift = p.nb - pbits - width;
     const uint32_t top = shift + width;   // <= 63
     const uint32_t mask = (1u << width) - 1u;
-    for (int i = t; i < (int)(mask + 1); i += kBlock) sh.rhist[i] = 0;
+    const uint32_t words = wide ? (mask + 1) + ((mask + 1) >> kWidePad) : mask + 1;
+    for (int i = t; i < (int)words; i += kBlock) hist[i] = 0;
     __syncthreads();
-    auto hist_fn = [&](bool valid, uint32_t k32, int32_t i) {
-      const uint64_t ck = p.key(k32, i);
-      hist_add(sh.rhist, valid && (ck >> top) == prefix, (uint32_t)(ck >> shift) & mask);
+    // Digits mix key and position bits, so hot bins are rare: plain atomics.
+    auto hist_fn = [&](bool valid, uint64_t ck) {
+      if (valid && (ck >> top) == prefix) {
+        const uint32_t d = (uint32_t)(ck >> shift) & mask;
+        atomicAdd(&hist[wide ? d + (d >> kWidePad) : d], 1u);
+      }
     };
-    if (in_list) ListSrc{sh.list, list_n}.each(hist_fn);
+    if (in_list) KeyListSrc{sh.list + list_off, list_n}.each(hist_fn);
     else src.each(hist_fn);
     __syncthreads();
     if (t == 0) sh.res[0] = kNotFound;
-    find_threshold<kRadixBins / kBlock>(sh.rhist, (int)(mask + 1), need, sh.scratch, sh.res);
-    if (sh.res[0] == kNotFound) {
+    if (wide) find_threshold<kFirstRadixBins / kBlock, kWidePad>(hist, (int)(mask + 1), need, sh.scratch, sh.res);
+    else find_threshold<kRadixBins / kBlock>(hist, (int)(mask + 1), need, sh.scratch, sh.res);
+    const uint32_t d = uni(sh.res[0]), above = uni(sh.res[1]), cnt = uni(sh.res[2]);
+    if (d == kNotFound) {
       if (t == 0) atomicOr(o.status, TOPK_DEVICE_INTERNAL);
       break;
     }
-    const uint32_t d = sh.res[0], above = sh.res[1], cnt = sh.res[2];
     const bool finish = cnt == need - above;
-    const bool compact = !SRC_IN_LDS && !in_list && !finish && cnt <= (uint32_t)kListCap;
-    if (t == 0) sh.cur_list = 0;
+    // compaction target: the whole list when the source lies outside LDS,
+    // else the free part before or after the current list
+    uint32_t target = 0;
+    bool compact = false;
+    if (!finish) {
+      if (!in_list) {
+        compact = cnt <= (uint32_t)kListCap;
+      } else if (list_off == 0) {
+        target = list_n;
+        compact = list_n + cnt <= (uint32_t)kListCap;
+      } else {
+        compact = cnt <= list_off;
+      }
+    }
+    if (t == 0) sh.cur_list = target;
     __syncthreads();
-    auto emit_fn = [&](bool valid, uint32_t k32, int32_t i) {
-      const uint64_t ck = p.key(k32, i);
+    auto emit_fn = [&](bool valid, uint64_t ck) {
       const bool m = valid && (ck >> top) == prefix;
       const uint32_t dig = (uint32_t)(ck >> shift) & mask;
-      emit_wave(m && (dig > d || (finish && dig == d)), i, &sh.cur_out, o);
-      if (compact) push_wave(m && dig == d, ((uint64_t)k32 << 32) | (uint32_t)i, &sh.cur_list, sh.list);
+      bad |= !emit_wave(m && (dig > d || (finish && dig == d)), p.pos(ck), &sh.cur_out, o);
+      if (compact) push_wave(m && dig == d, ck, &sh.cur_list, sh.list);
     };
-    if (in_list) ListSrc{sh.list, list_n}.each(emit_fn);
+    if (in_list) KeyListSrc{sh.list + list_off, list_n}.each(emit_fn);
     else src.each(emit_fn);
     __syncthreads();
     if (finish) break;
@@ -589,36 +735,138 @@ __device__ __forceinline__ void refine(const Src& src, const Refine& p, Smem& sh
     pbits += width;
     if (compact) {
       in_list = true;
+      list_off = target;
       list_n = cnt;
     }
   }
+  report_bad(bad, o.status);
 }
 
-// Out-of-line refinement for the sources outside LDS, so their code does not
-// sit in the register-resident path.
-template <bool VEC>
-__device__ __forceinline__ void refine_stream(const float* rowp, int32_t begin, int32_t end, Cut cut,
-                                                        const Refine p, Smem& sh, const RowOut o) {
-  refine<false>(StreamSrc<VEC>{rowp, begin, end, cut}, p, sh, o);
+template <bool SRC_IN_LDS, class Src>
+__device__ __forceinline__ void refine(const Src& src, const Refine& p, Smem& sh, const RowOut& o) {
+  refine<SRC_IN_LDS>(src, p, sh, o, 0ull, 0u, p.need, p.cnt);
 }
 
-__device__ __forceinline__ void refine_global(const uint64_t* list, uint32_t n, const Refine p, Smem& sh,
-                                                        const RowOut o) {
-  refine<false>(ListSrc{list, n}, p, sh, o);
+// First refinement pass over n <= J * kBlock boundary candidates held in
+// registers as 32-bit key offsets kd (FP32 key minus the smallest candidate
+// key) and positions (lane t holds entries j * kBlock + t). The digit is 13
+// bits for large sets, 11 for small ones; it comes from kd alone when the
+// key range is at least that wide (the composite key's top bits are then key
+// bits), else from the composite key. Its histogram, padded one word per
+// lane-group so the threshold scan is bank-conflict free, lives in the (free)
+// LDS list region; emission and compaction offsets come from one block scan
+// of per-lane counts. Survivors continue in LDS as composite keys.
+template <int J>
+__device__ __forceinline__ void resolve_regs(const uint32_t (&kd)[J], const uint32_t (&ps)[J], uint32_t n,
+                                             const Refine& p, Smem& sh, const RowOut& o) {
+  const int t = threadIdx.x;
+  const bool wide = n > 4096u;
+  const uint32_t b1 = p.nb - p.b2;
+  const uint32_t width = min(wide ? (uint32_t)kFirstRadixBits : (uint32_t)kRadixBits, p.nb);
+  const uint32_t shift = p.nb - width;
+  const uint32_t mask = (1u << width) - 1u;
+  const uint32_t pad = wide ? 4u : 2u;   // log2 of the bins each lane scans
+  const bool key_only = b1 >= width;     // digit = kd >> (b1 - width)
+  // lane t holds nv valid entries: j * kBlock + t < n  <=>  j < nv
+  const int nv = (int)((n + kBlock - 1 - (uint32_t)t) / kBlock);
+  auto digit = [&](int j) -> uint32_t {
+    if (key_only) return kd[j] >> (b1 - width);
+    const uint64_t ck = ((uint64_t)kd[j] << p.b2) | (uint64_t)(p.idx_hi - ps[j]);
+    return (uint32_t)(ck >> shift) & mask;
+  };
+  uint32_t* hist = reinterpret_cast<uint32_t*>(sh.list);
+  const uint32_t words = (mask + 1) + ((mask + 1) >> pad);
+  for (int i = t; i < (int)words; i += kBlock) hist[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (j < nv) {
+      const uint32_t d = digit(j);
+      atomicAdd(&hist[d + (d >> pad)], 1u);
+    }
+  }
+  __syncthreads();
+  if (t == 0) sh.res[0] = kNotFound;
+  if (wide) find_threshold<kFirstRadixBins / kBlock, 4>(hist, (int)(mask + 1), p.need, sh.scratch, sh.res);
+  else find_threshold<kRadixBins / kBlock, 2>(hist, (int)(mask + 1), p.need, sh.scratch, sh.res);
+  const uint32_t d = uni(sh.res[0]), above = uni(sh.res[1]), cnt = uni(sh.res[2]);
+  if (d == kNotFound) {
+    if (t == 0) atomicOr(o.status, TOPK_DEVICE_INTERNAL);
+    return;
+  }
+  const bool finish = cnt == p.need - above;
+  const uint32_t dlo = finish ? d : d + 1;   // emitted: digit >= dlo; kept: digit == d (unless finish)
+  uint32_t na = 0, nk = 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const uint32_t dj = digit(j);
+    na += (j < nv && dj >= dlo) ? 1u : 0u;
+    nk += (j < nv && dj == d) ? 1u : 0u;
+  }
+  if (finish) nk = 0;
+  const uint32_t base = uni(sh.cur_out);
+  uint32_t tot;
+  const uint32_t off = block_exclusive_add((nk << 16) | na, sh.scratch, &tot);   // counts < 2^16
+  uint32_t ao = base + (off & 0xFFFFu), ko = off >> 16;
+  bool bad = false;
+  if (na | nk) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const uint32_t dj = digit(j);
+      if (j < nv && dj >= dlo) bad |= !o.write(ao++, (int32_t)ps[j]);
+      if (!finish && j < nv && dj == d) sh.list[ko++] = p.key(kd[j] + p.lo32, (int32_t)ps[j]);
+    }
+  }
+  report_bad(bad, o.status);
+  __syncthreads();
+  if (t == 0) sh.cur_out = base + (tot & 0xFFFFu);
+  __syncthreads();
+  if (finish) return;
+  refine<true>(KeyListSrc{sh.list, cnt}, p, sh, o, (uint64_t)d, width, p.need - above, cnt);
+}
+
+// Register slots per lane for n register-resident candidates.
+constexpr int kRegSmall = 2, kRegMid = 8;
+static_assert(kRegMid < kResolveRegs, "slot classes grow");
+
+// Rewrite the LDS pair list sh.list[0, n) as composite keys, in place.
+__device__ __forceinline__ void pairs_to_keys(Smem& sh, uint32_t n, const Refine& p) {
+  for (uint32_t i = threadIdx.x; i < n; i += kBlock) {
+    const uint64_t e = sh.list[i];
+    sh.list[i] = p.key((uint32_t)(e >> 32), (int32_t)(uint32_t)e);
+  }
+  __syncthreads();
+}
+
+// The pair list sh.list[0, n) (n <= J * kBlock) into registers, then the
+// register-resident first pass.
+template <int J>
+__device__ __forceinline__ void resolve_lds_pairs(uint32_t n, const Refine& p, Smem& sh, const RowOut& o) {
+  uint32_t kd[J], ps[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const uint32_t i = (uint32_t)j * kBlock + threadIdx.x;
+    const uint64_t v = i < n ? sh.list[i] : 0ull;
+    kd[j] = (uint32_t)(v >> 32) - p.lo32;
+    ps[j] = (uint32_t)v;
+  }
+  __syncthreads();
+  resolve_regs<J>(kd, ps, n, p, sh, o);
 }
 
 // A row the workgroup owns alone: register path when the row fits one tile,
-// streaming path otherwise.
+// streaming path otherwise. Selected positions are staged in LDS and the
+// row's k outputs flushed once at the end.
 template <bool VEC>
 __device__ __forceinline__ void owned_row(const SelectArgs& a, int32_t len, const float* rowp, const RowOut& o,
                                           bool resident, uint32_t (&hk)[kHk], Smem& sh) {
   if (threadIdx.x == 0) sh.res[0] = kNotFound;
   find_threshold_raw(sh.lhist, (uint32_t)a.k, sh.scratch, sh.res);
-  if (sh.res[0] == kNotFound) {  // fewer valid scores than k: NaN inputs
+  const uint32_t bstar = uni(sh.res[0]), n_above = uni(sh.res[1]), cnt = uni(sh.res[2]);
+  if (bstar == kNotFound) {  // fewer valid scores than k: NaN inputs
     if (threadIdx.x == 0) atomicOr(a.status, TOPK_DEVICE_INTERNAL);
     return;
   }
-  const uint32_t bstar = sh.res[0], n_above = sh.res[1], cnt = sh.res[2];
   const Cut cut = cut_of_bin(bstar);
   const bool use_list = cnt <= (uint32_t)kListCap;
   if (threadIdx.x == 0) {
@@ -628,20 +876,115 @@ __device__ __forceinline__ void owned_row(const SelectArgs& a, int32_t len, cons
   }
   __syncthreads();
   Range rg;
-  uint64_t* dst = use_list ? sh.list : nullptr;
+  bool bad = false;
+  auto on_above = [&](int32_t e, int32_t) { bad |= !o.write(atomicAdd(&sh.cur_out, 1u), e); };
+  auto on_cand = [&](uint32_t kk, int32_t e) {
+    if (use_list) {
+      const uint32_t c = atomicAdd(&sh.cur_list, 1u);
+      const bool ok = c < (uint32_t)kListCap;
+      if (ok) sh.list[c] = ((uint64_t)kk << 32) | (uint32_t)e;
+      bad |= !ok;
+    }
+  };
   if (resident) {
-    extract(interest_mask(hk, cut.vlo), 0, rowp, cut.vhi, &sh.cur_out, o, &sh.cur_list, dst, kListCap, rg);
+    extract(interest_mask(hk, cut.vlo), 0, rowp, cut.vhi, rg, on_above, on_cand);
   } else {
     for (int32_t base = 0; base < len; base += kTile) {
       load_pack<VEC>(rowp, base, len, hk);
-      extract(interest_mask(hk, cut.vlo), base, rowp, cut.vhi, &sh.cur_out, o, &sh.cur_list, dst, kListCap, rg);
+      extract(interest_mask(hk, cut.vlo), base, rowp, cut.vhi, rg, on_above, on_cand);
     }
   }
   merge_range(rg, sh);
+  report_bad(bad, a.status);
   __syncthreads();
   const Refine p = make_refine(sh.range, (uint32_t)a.k - n_above, cnt);
-  if (use_list) refine<true>(ListSrc{sh.list, cnt}, p, sh, o);
-  else refine_stream<VEC>(rowp, 0, len, cut, p, sh, o);
+  if (use_list && cnt <= (uint32_t)(kRegSmall * kBlock)) {
+    resolve_lds_pairs<kRegSmall>(cnt, p, sh, o);
+  } else if (use_list && cnt <= (uint32_t)(kRegMid * kBlock)) {
+    resolve_lds_pairs<kRegMid>(cnt, p, sh, o);
+  } else if (use_list && cnt <= (uint32_t)(kResolveRegs * kBlock)) {
+    resolve_lds_pairs<kResolveRegs>(cnt, p, sh, o);
+  } else if (use_list) {
+    pairs_to_keys(sh, cnt, p);
+    refine<true>(KeyListSrc{sh.list, cnt}, p, sh, o);
+  } else {
+    refine<false>(StreamSrc<VEC>{rowp, 0, len, cut, p}, p, sh, o);
+  }
+  report_bad(!o.flush(0, (uint32_t)a.k), a.status);
+}
+
+// The last workgroup of a split row resolves its threshold bin from the
+// candidates the row's workgroups left in global memory, then flushes the
+// outputs [n_above, k). The candidate range and (when they fit the
+// registers) the candidates are fetched in one round trip.
+// Candidates [0, n) of a split row's global list (n <= J * kBlock) and the
+// row's candidate range, fetched in one round trip; then the register pass.
+template <int J>
+__device__ __forceinline__ void resolve_global_regs(const GroupState* g, const uint64_t* slab, uint32_t need,
+                                                    uint32_t n, Smem& sh, const RowOut& o) {
+  const int t = threadIdx.x;
+  uint64_t e[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const uint32_t i = (uint32_t)j * kBlock + t;
+    e[j] = i < n ? ld_agent(slab + i) : 0ull;
+  }
+  if (t < 4) sh.range[t] = ld_agent(&g->range[t]);
+  __syncthreads();
+  const Refine p = make_refine(sh.range, need, n);
+  uint32_t kd[J], ps[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    kd[j] = (uint32_t)(e[j] >> 32) - p.lo32;
+    ps[j] = (uint32_t)e[j];
+  }
+  resolve_regs<J>(kd, ps, n, p, sh, o);
+}
+
+// The last workgroup of a split row resolves its threshold bin from the
+// candidates the row's workgroups left in global memory, then flushes the
+// outputs [n_above, k).
+template <bool VEC>
+__device__ __forceinline__ void resolve_split(const SelectArgs& a, const GroupState* g, const uint64_t* slab,
+                                              bool keep, int32_t len, const float* rowp, Cut cut, uint32_t need,
+                                              uint32_t cnt, uint32_t n_above, Smem& sh, const RowOut& o) {
+  const int t = threadIdx.x;
+  if (t == 0) sh.cur_out = n_above;
+  if (keep && cnt <= (uint32_t)(kRegSmall * kBlock)) {
+    resolve_global_regs<kRegSmall>(g, slab, need, cnt, sh, o);
+  } else if (keep && cnt <= (uint32_t)(kRegMid * kBlock)) {
+    resolve_global_regs<kRegMid>(g, slab, need, cnt, sh, o);
+  } else if (keep && cnt <= (uint32_t)(kResolveRegs * kBlock)) {
+    resolve_global_regs<kResolveRegs>(g, slab, need, cnt, sh, o);
+  } else {
+    if (t < 4) sh.range[t] = ld_agent(&g->range[t]);
+    __syncthreads();
+    const Refine p = make_refine(sh.range, need, cnt);
+    if (!keep) {
+      refine<false>(StreamSrc<VEC>{rowp, 0, len, cut, p}, p, sh, o);
+    } else if (cnt <= (uint32_t)kListCap) {
+      // Pull the list into LDS as composite keys, kLoadBatch device-coherent
+      // loads in flight per lane, then resolve it there.
+      for (uint32_t i0 = 0; i0 < cnt; i0 += kLoadBatch * kBlock) {
+        uint64_t b[kLoadBatch];
+#pragma unroll
+        for (int j = 0; j < kLoadBatch; ++j) {
+          const uint32_t i = i0 + (uint32_t)j * kBlock + t;
+          b[j] = i < cnt ? ld_agent(slab + i) : 0ull;
+        }
+#pragma unroll
+        for (int j = 0; j < kLoadBatch; ++j) {
+          const uint32_t i = i0 + (uint32_t)j * kBlock + t;
+          if (i < cnt) sh.list[i] = p.key((uint32_t)(b[j] >> 32), (int32_t)(uint32_t)b[j]);
+        }
+      }
+      __syncthreads();
+      refine<true>(KeyListSrc{sh.list, cnt}, p, sh, o);
+    } else {
+      refine<false>(PairListSrc{slab, cnt, p}, p, sh, o);
+    }
+  }
+  report_bad(!o.flush(n_above, o.k), o.status);
 }
 
 // A row shared by w.gsize workgroups; this one holds chunk [w.begin, end).
@@ -659,7 +1002,7 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
   if ((uint32_t)(end - begin) >= k) {
     if (t == 0) sh.res[0] = 0;
     find_threshold_raw(sh.lhist, k, sh.scratch, sh.res);
-    bloc = sh.res[0];
+    bloc = uni(sh.res[0]);
   }
   for (int r = t; r < kBins; r += kBlock) {
     const uint32_t h = sh.lhist[r];
@@ -667,13 +1010,13 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
     if (h && b >= bloc && b >= kFirstBin && b <= kLastBin)
       __hip_atomic_fetch_add(&g->hist[r], h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  drain_memory();
   __syncthreads();
   if (t == 0) {
-    __hip_atomic_fetch_add(&g->arrive, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(&g->arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t spins = 0, ok = 1;
-    while (__hip_atomic_load(&g->arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < G) {
-      __builtin_amdgcn_s_sleep(2);
+    while (ld_agent(&g->arrive) < G) {
+      __builtin_amdgcn_s_sleep(1);
       if (++spins > a.spin_limit) {
         ok = 0;
         break;
@@ -683,21 +1026,20 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
     sh.flag = ok;
   }
   __syncthreads();
-  if (!sh.flag) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  for (int r = t; r < kBins; r += kBlock)
-    sh.rhist[r] = __hip_atomic_load(&g->hist[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (!uni(sh.flag)) return;
+  for (int r = t; r < kBins; r += kBlock) sh.rhist[r] = ld_agent(&g->hist[r]);
   __syncthreads();
   // Bins at or above the largest chunk threshold are complete, and the row's
-  // threshold bin lies there, so the scan from the top is exact.
+  // threshold bin lies there, so the scan from the top is exact. Not found
+  // only with NaN inputs; the workgroup then skips its emission but still
+  // takes part in the arrival count so the row's state is reset.
   if (t == 0) sh.res[0] = kNotFound;
   find_threshold_raw(sh.rhist, k, sh.scratch, sh.res);
-  // Not found only with NaN inputs; the workgroup then skips its emission but
-  // still takes part in the arrival count so the row's state is reset.
-  const bool found = sh.res[0] != kNotFound;
+  const uint32_t r0 = uni(sh.res[0]);
+  const bool found = r0 != kNotFound;
   if (!found && t == 0) atomicOr(a.status, TOPK_DEVICE_INTERNAL);
-  const uint32_t bstar = found ? sh.res[0] : kLastBin;
-  const uint32_t n_above = found ? sh.res[1] : 0u, cnt = found ? sh.res[2] : 0u;
+  const uint32_t bstar = found ? r0 : kLastBin;
+  const uint32_t n_above = found ? uni(sh.res[1]) : 0u, cnt = found ? uni(sh.res[2]) : 0u;
   const Cut cut = cut_of_bin(bstar);
   uint32_t la = 0;
   for (int r = t; r < kBins; r += kBlock) {
@@ -706,36 +1048,59 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
   }
   uint32_t local_above;
   block_exclusive_add(la, sh.scratch, &local_above);
-  const uint32_t local_cnt = found ? sh.lhist[raw_of_bin(bstar)] : 0u;
+  local_above = uni(local_above);
+  const uint32_t local_cnt = found ? uni(sh.lhist[raw_of_bin(bstar)]) : 0u;
   const bool keep = found && (int64_t)cnt <= a.cand_cap;
+  const bool stage = keep && local_cnt <= (uint32_t)kListCap;   // candidates staged in LDS
+  // This workgroup's output and candidate offsets in the row; their round
+  // trips overlap the re-reads of the extraction below.
   uint32_t base_out = 0, base_cand = 0;
   if (t == 0) {
     if (local_above) base_out = __hip_atomic_fetch_add(&g->emit, local_above, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (keep && local_cnt) base_cand = __hip_atomic_fetch_add(&g->cand, local_cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  // the interest mask overlaps the two atomics' round trip
-  const uint32_t mask0 = (resident && found) ? interest_mask(hk, cut.vlo) : 0u;
-  if (t == 0) {
-    sh.cur_out = base_out;
-    sh.cur_list = base_cand;
+    sh.cur_out = 0;
+    sh.cur_list = (keep && !stage) ? base_cand : 0u;
     sh.range[0] = sh.range[1] = sh.range[2] = sh.range[3] = 0;
   }
   __syncthreads();
   uint64_t* slab = a.cand + (int64_t)w.group * a.cand_cap;
-  uint64_t* dst = keep ? slab : nullptr;
+  uint32_t* staged = sh.rhist;     // positions above the threshold bin (< k of them)
+  uint32_t* staged_pg = sh.outpos; // and their block-table entries
   Range rg;
-  if (resident) {
-    extract(mask0, begin, rowp, cut.vhi, &sh.cur_out, o, &sh.cur_list, dst, (uint32_t)a.cand_cap, rg);
-  } else if (found) {
-    for (int32_t base = begin; base < end; base += kTile) {
-      load_pack<VEC>(rowp, base, end, hk);
-      extract(interest_mask(hk, cut.vlo), base, rowp, cut.vhi, &sh.cur_out, o, &sh.cur_list, dst,
-              (uint32_t)a.cand_cap, rg);
+  bool bad = false;
+  auto on_above = [&](int32_t e, int32_t pg) {
+    const uint32_t c = atomicAdd(&sh.cur_out, 1u);
+    const bool ok = c < (uint32_t)kMaxK;
+    if (ok) {
+      staged[c] = (uint32_t)e;
+      staged_pg[c] = (uint32_t)pg;
+    }
+    bad |= !ok;
+  };
+  auto on_cand = [&](uint32_t kk, int32_t e) {
+    if (!keep) return;
+    const uint32_t c = atomicAdd(&sh.cur_list, 1u);
+    const uint64_t v = ((uint64_t)kk << 32) | (uint32_t)e;
+    const bool ok = stage ? c < (uint32_t)kListCap : (int64_t)c < a.cand_cap;
+    if (ok && stage) sh.list[c] = v;
+    if (ok && !stage) st_agent(slab + c, v);
+    bad |= !ok;
+  };
+  if (found) {
+    if (resident) {
+      extract(interest_mask(hk, cut.vlo), begin, rowp, cut.vhi, rg, on_above, on_cand, &o);
+    } else {
+      for (int32_t base = begin; base < end; base += kTile) {
+        load_pack<VEC>(rowp, base, end, hk);
+        extract(interest_mask(hk, cut.vlo), base, rowp, cut.vhi, rg, on_above, on_cand, &o);
+      }
     }
   }
   merge_range(rg, sh);
   __syncthreads();
   if (t == 0) {
+    sh.bcast[0] = base_out;
+    sh.bcast[1] = base_cand;
     if (local_cnt) {
       __hip_atomic_fetch_max(&g->range[0], sh.range[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_fetch_max(&g->range[1], sh.range[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -743,33 +1108,38 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
       __hip_atomic_fetch_max(&g->range[3], sh.range[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  // Staged outputs and candidates leave in consecutive, coalesced stores.
+  const uint32_t bo = uni(sh.bcast[0]), bc = uni(sh.bcast[1]);
+  const uint32_t n_out = min(uni(sh.cur_out), (uint32_t)kMaxK);
+  for (uint32_t i = t; i < n_out; i += kBlock) bad |= !o.store_page(bo + i, (int32_t)staged[i], (int32_t)staged_pg[i]);
+  if (stage) {
+    const uint32_t n_c = min(uni(sh.cur_list), (uint32_t)kListCap);
+    for (uint32_t i = t; i < n_c; i += kBlock) {
+      const bool ok = (int64_t)(bc + i) < a.cand_cap;
+      if (ok) st_agent(slab + bc + i, sh.list[i]);
+      bad |= !ok;
+    }
+  }
+  report_bad(bad, a.status);
+  drain_memory();
   __syncthreads();
   if (t == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(&g->done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t prev = __hip_atomic_fetch_add(&g->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sh.flag = prev == G - 1;
   }
   __syncthreads();
-  if (!sh.flag) return;
-  // Last workgroup of the row: resolve the threshold bin.
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  if (t < 4) sh.range[t] = __hip_atomic_load(&g->range[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (t == 0) sh.cur_out = n_above;
-  __syncthreads();
-  const Refine p = make_refine(sh.range, k - n_above, cnt);
-  if (!found) {
-  } else if (keep) {
-    refine_global(slab, cnt, p, sh, o);
-  } else {
-    refine_stream<VEC>(rowp, 0, len, cut, p, sh, o);
-  }
-  for (int r = t; r < kBins; r += kBlock) __hip_atomic_store(&g->hist[r], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (t < 4) __hip_atomic_store(&g->range[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (!uni(sh.flag)) return;
+  // Last workgroup of the row: resolve the threshold bin, then leave the
+  // row's state zeroed for the next call.
+  if (found) resolve_split<VEC>(a, g, slab, keep, len, rowp, cut, k - n_above, cnt, n_above, sh, o);
+  for (int r = t; r < kBins; r += kBlock) st_agent(&g->hist[r], 0u);
+  if (t < 4) st_agent(&g->range[t], 0u);
   if (t == 0) {
-    __hip_atomic_store(&g->arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&g->emit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&g->cand, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&g->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    st_agent(&g->arrive, 0u);
+    st_agent(&g->emit, 0u);
+    st_agent(&g->cand, 0u);
+    st_agent(&g->done, 0u);
   }
 }
 
@@ -777,7 +1147,7 @@ template <bool VEC>
 __device__ __forceinline__ void process_item(const SelectArgs& a, const WorkItem& w, Smem& sh) {
   const int t = threadIdx.x;
   const int row = w.row;
-  const int32_t len = a.lengths[row];
+  const int32_t len = w.len;   // planned from the same lengths (one dependent load fewer)
   if (len < 0 || (int64_t)len > a.max_len) {
     if (t == 0) atomicOr(a.status, TOPK_DEVICE_BAD_LENGTH);
     return;
@@ -789,12 +1159,14 @@ __device__ __forceinline__ void process_item(const SelectArgs& a, const WorkItem
   o.ps = a.page_size;
   o.shift = a.page_shift;
   o.k = (uint32_t)a.k;
+  o.len = (uint32_t)len;
   o.status = a.status;
+  o.stage = sh.outpos;
   if (len <= a.k) {  // every valid position is selected; pad with -1
     if (w.begin == 0) {
       for (int j = t; j < a.k; j += kBlock) {
         if (j < len) {
-          o.write((uint32_t)j, j);
+          o.store((uint32_t)j, j);
         } else {
           o.slots[j] = -1;
           if (o.idx) o.idx[j] = -1;
@@ -824,15 +1196,19 @@ __device__ __forceinline__ void process_item(const SelectArgs& a, const WorkItem
 }
 
 template <bool VEC>
-__global__ void __launch_bounds__(kBlock, 4) topk_select_kernel(SelectArgs a) {
+__global__ void __launch_bounds__(kBlock) topk_select_kernel(SelectArgs a) {
   __shared__ Smem sh;
+  // The first item is fetched together with the header (the plan buffer
+  // always holds at least gridDim.x items, so the read stays in bounds; the
+  // item is used only if the header says it exists).
+  const WorkItem first = a.items[blockIdx.x];
   const PlanHeader h = *a.plan;
   if (h.magic != kPlanMagic || h.k != a.k || h.grid != (int)gridDim.x || h.num_rows > a.num_rows) {
     if (threadIdx.x == 0 && blockIdx.x == 0) atomicOr(a.status, TOPK_DEVICE_PLAN_MISMATCH);
     return;
   }
   for (int it = blockIdx.x; it < h.num_items; it += gridDim.x) {
-    const WorkItem w = a.items[it];
+    const WorkItem w = it == (int)blockIdx.x ? first : a.items[it];
     process_item<VEC>(a, w, sh);
     __syncthreads();
   }

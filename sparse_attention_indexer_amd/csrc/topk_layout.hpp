@@ -7,21 +7,23 @@
 
 namespace satopk {
 
-// Workgroup shape. 512 lanes = 8 wave64s; every lane holds kEpt scores of a
-// register-resident tile (kEpt / 4 dwordx4 loads in flight per lane).
+// Workgroup shape: one 512-lane workgroup (8 wave64s) per CU, so it may use
+// up to 256 VGPRs and most of the CU's 160 KB of LDS. Every lane holds kEpt
+// scores of a register-resident tile as packed FP16 (kEpt / 4 dwordx4 loads
+// in flight per lane, 128 KB per CU).
 constexpr int kBlock = 512;
 constexpr int kWaves = kBlock / 64;
-constexpr int kEpt = 32;
-constexpr int kTile = kBlock * kEpt;          // 16,384 scores = 64 KB per tile
+constexpr int kEpt = 64;
+constexpr int kTile = kBlock * kEpt;          // 32,768 scores = 128 KB per tile
 
 constexpr int kMaxK = 2048;
 constexpr int kBins = 1024;                   // top 10 bits of the 16-bit ordered key
 constexpr int kRadixBits = 11;                // digit width of the exact refinement
 constexpr int kRadixBins = 1 << kRadixBits;
-constexpr int kListCap = 4096;                // boundary survivors kept in LDS
+constexpr int kListCap = 16384;               // boundary candidates kept in LDS (128 KB)
 constexpr int kChunkAlign = 256;              // chunk starts are multiples of this
 constexpr int kDefaultMinChunk = 4096;
-constexpr int kDefaultCandCap = 16384;        // boundary candidates per split row
+constexpr int kDefaultCandCap = kListCap;     // boundary candidates per split row (fits the resolver's LDS)
 
 constexpr uint32_t kPlanMagic = 0x31504B54u;  // "TKP1"
 constexpr uint32_t kDefaultSpinLimit = 1u << 21;
@@ -46,7 +48,8 @@ struct WorkItem {
   int32_t end;
   int32_t group;   // -1: the workgroup owns the whole row; else split-row slot
   int32_t gsize;   // workgroups sharing the row (1 for an owned row)
-  int32_t pad[3];
+  int32_t len;     // the row's valid length as planned (-1: outside [0, max_len])
+  int32_t pad[2];
 };
 static_assert(sizeof(WorkItem) == 32, "work item is 32 bytes");
 

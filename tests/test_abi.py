@@ -46,7 +46,7 @@ def test_status_strings(T):
 
 
 def test_register_capacity(T):
-    assert T.topk_register_capacity() == 16384
+    assert T.topk_register_capacity() == 32768
 
 
 @pytest.mark.parametrize("kw", [
@@ -72,7 +72,7 @@ def test_reserved_must_be_zero(T):
 
 
 def test_register_path_too_long_is_unsupported(T):
-    cfg = T.make_config(2048, 2, 16385, force_path="register")
+    cfg = T.make_config(2048, 2, 32769, force_path="register")
     with pytest.raises(T.TopKError) as e:
         T.topk_query_sizes(cfg)
     assert e.value.status == T.TOPK_ERR_UNSUPPORTED
