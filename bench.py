@@ -11,7 +11,7 @@ the same run and reported beside it.
 Inputs are resident in HBM before timing starts, and each step reads a
 different copy out of a rotation of at least 512 MB (twice the 256 MB
 Infinity Cache), so the scores come from HBM rather than cache. Prints one
-JSON line.
+JSON line (``--sweep`` prints one per workload instead).
 """
 from __future__ import annotations
 
@@ -20,6 +20,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -29,11 +30,22 @@ if ROOT not in sys.path:
 
 METRIC = "TopK latency (µs) at 7×80K and 7×1M, k=2048; HBM GB/s vs peak"
 PEAK_HBM_GBS = 8000.0
-PAGES_V2_1M_US = 36.6     # the page's TopK-V2 latency at 1M ISL (B300; context only)
+PAGES_V2_US = {"7x1m": 36.6, "7x80k": 17.5}   # the page's TopK-V2 latencies (B300; context only)
 ROTATION_BYTES = 512 << 20
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "select_c3_7x1m_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "topk_select_kernel_7x1m_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "sparse_attention_indexer_amd", "csrc", f)
                   for f in ("topk_kernels.hip", "topk_device.hpp", "topk_layout.hpp")]
+
+DESCRIPTIONS = {
+    "7x1m": "7x1M k=2048: 7 rows x 1,000,000 FP32 scores ~N(0,1), 1% in [3.0,3.0005), "
+            "64-token pages, shared random page permutation",
+    "7x80k": "7x80K k=2048: 7 rows x 80,000 FP32 scores (30% exact zeros, rest 2|N(0,1)|), "
+             "valid length 79,994+r, -inf tail, 64-token pages, shared random page permutation",
+}
+
+
+def say(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
 
 
 def kernel_source_digest() -> str:
@@ -41,6 +53,14 @@ def kernel_source_digest() -> str:
     for p in KERNEL_SOURCES:
         h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
+
+
+def workload(name: str):
+    import synth
+    table = {"7x1m": 3, "7x80k": 2, "c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5}
+    if name == "cp8_7x125k":
+        return synth.make_cp_shard()
+    return synth.make_config(table[name])
 
 
 def algorithmic_bytes(w, slots, with_idx: bool) -> int:
@@ -59,14 +79,23 @@ def algorithmic_bytes(w, slots, with_idx: bool) -> int:
 
 
 def measure(w, steps: int, warmup: int, with_idx: bool = True, rotate: bool = True):
-    """Time `steps` plan+select steps; returns a dict of timings and the last output."""
+    """Time `steps` plan+select steps; returns a dict of timings and the last output.
+
+    Two passes of `steps` steps each. The first is the timed region proper:
+    nothing but the steps between two synchronisations (wall clock per step).
+    The second records HIP events: stream events around the planning kernel
+    and the selection call, on the stream both are launched on (torch's current
+    stream, which the binding passes to the library), and the selection
+    kernel's own start and end (topk_select_paged_timed), the interval a
+    kernel trace reports. Recording events adds work between launches, so
+    they stay out of the wall-clock pass."""
     import numpy as np
     import torch
     from sparse_attention_indexer_amd import topk
 
     dev = torch.device("cuda:0")
-    tk = topk.TopK(w.k, w.rows, w.max_len, device=dev)
-    per_copy = w.scores.nbytes
+    tk = topk.TopK(w.k, w.rows, max(1, w.max_len), device=dev)
+    per_copy = max(1, w.scores.nbytes)
     ncopy = max(1, math.ceil(ROTATION_BYTES / per_copy)) if rotate else 1
     base = torch.from_numpy(np.ascontiguousarray(w.scores)).to(dev)
     copies = [base] + [base.clone() for _ in range(ncopy - 1)]
@@ -83,38 +112,63 @@ def measure(w, steps: int, warmup: int, with_idx: bool = True, rotate: bool = Tr
         if ev is not None:
             ev[1].record(stream)
         tk.select(copies[i % ncopy], lengths, table, w.bt_row_stride, w.page_size,
-                  out_slots=slots, out_indices=idx, with_indices=with_idx)
+                  out_slots=slots, out_indices=idx, with_indices=with_idx,
+                  events=None if ev is None else (ev[3], ev[4]))
         if ev is not None:
             ev[2].record(stream)
 
     for i in range(warmup):
         step(i)
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for e in evs:   # create the kernel-event pair's HIP events before timing
+        e[3].record(stream)
+        e[4].record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(i, evs[i])
+        step(warmup + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    for i in range(steps):
+        step(warmup + steps + i, evs[i])
+    torch.cuda.synchronize()
     st = tk.status()
     if st != 0:
         raise RuntimeError(f"device status {st}")
     plan_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    sel_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    # last step's input copy, for the parity check
-    last = (steps - 1) % ncopy
-    return {
+    sel_ms = [e[3].elapsed_time(e[4]) for e in evs]
+    sel_stream_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    last = (warmup + 2 * steps - 1) % ncopy
+    out = (None if idx is None else idx.cpu().numpy(), slots.cpu().numpy())
+    res = {
         "ms_per_step": (t1 - t0) * 1e3 / steps,
         "select_ms": float(np.mean(sel_ms)),
         "select_p50_ms": float(np.median(sel_ms)),
         "select_p10_ms": float(np.percentile(sel_ms, 10)),
         "select_p90_ms": float(np.percentile(sel_ms, 90)),
         "plan_ms": float(np.mean(plan_ms)),
+        "select_stream_ms": float(np.mean(sel_stream_ms)),
         "copies": ncopy,
-        "out": (None if idx is None else idx.cpu().numpy(), slots.cpu().numpy()),
+        "out": out,
         "last_copy_equal": bool(torch.equal(copies[last], base)),
     }
+    del copies, base
+    torch.cuda.empty_cache()
+    return res
+
+
+def calibrate_copy(mib: int, reps: int = 3) -> None:
+    """A plain device-to-device copy of `mib` MiB, `reps` times: the known-size
+    kernel that scales the HBM byte counters."""
+    import torch
+    n = mib << 18
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    say(f"[bench] copy calibration: {reps} x {mib} MiB device-to-device")
 
 
 def cpu_baseline(w, seconds: float):
@@ -130,9 +184,65 @@ def cpu_baseline(w, seconds: float):
         if time.perf_counter() - t0 >= seconds or reps >= 50:
             break
     dt = time.perf_counter() - t0
-    return {"value": dt / reps * 1e6, "unit": "µs", "cores": threads, "kind": "oracle",
+    return {"value": round(dt / reps * 1e6, 1), "unit": "µs", "cores": threads, "kind": "oracle",
             "sample": f"{reps} full batches of {w.rows}x{w.stride} (full sort per row, "
                       f"{threads} threads, one row range each)"}, result
+
+
+def matches(got, want) -> bool:
+    import numpy as np
+    import oracle
+    g, r = oracle.canonical(*got), oracle.canonical(*want)
+    return bool(np.array_equal(g[0], r[0]) and np.array_equal(g[1], r[1]))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def sweep(args) -> int:
+    """One JSON line per workload: latency percentiles, rows/s, algorithmic GB/s,
+    plan time, parity and the oracle's wall time (1 thread and N threads)."""
+    import oracle
+    ok = True
+    names = args.sweep.split(",")
+    for name in names:
+        w = workload(name)
+        say(f"[bench] sweep {name}: {w.rows}x{w.stride}")
+        res = measure(w, args.steps, args.warmup, rotate=not args.warm_cache)
+        nthreads = min(w.rows, os.cpu_count() or 1)
+        t1, tn = [], []
+        ref = None
+        for _ in range(3):
+            t = time.perf_counter()
+            ref = oracle.topk_workload(w, threads=1)
+            t1.append(time.perf_counter() - t)
+            t = time.perf_counter()
+            oracle.topk_workload(w, threads=nthreads)
+            tn.append(time.perf_counter() - t)
+        parity = matches(res["out"], ref) and res["last_copy_equal"]
+        ok &= parity
+        nbytes = algorithmic_bytes(w, res["out"][1], True)
+        p50 = res["select_p50_ms"] * 1e-3
+        print(json.dumps({
+            "workload": w.name, "rows": w.rows, "stride": w.stride, "k": w.k,
+            "select_us": {"p50": round(res["select_p50_ms"] * 1e3, 3), "p10": round(res["select_p10_ms"] * 1e3, 3),
+                          "p90": round(res["select_p90_ms"] * 1e3, 3), "mean": round(res["select_ms"] * 1e3, 3)},
+            "plan_us": round(res["plan_ms"] * 1e3, 3), "step_us": round(res["ms_per_step"] * 1e3, 3),
+            "rows_per_s": round(w.rows / p50), "algorithmic_bytes": nbytes,
+            "gbs": round(nbytes / p50 / 1e9, 1), "frac_of_8tbs": round(nbytes / p50 / 1e9 / PEAK_HBM_GBS, 4),
+            "cache": "warm" if args.warm_cache else f"cold ({res['copies']} copies)",
+            "oracle_1thread_s": round(statistics.median(t1), 4),
+            f"oracle_{nthreads}threads_s": round(statistics.median(tn), 4),
+            "cpu": cpu_model(), "nproc": os.cpu_count(), "parity": parity,
+        }), flush=True)
+    return 0 if ok else 1
 
 
 def main() -> int:
@@ -140,42 +250,53 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workloads", default="7x1m,7x80k",
+                    help="comma list from {7x1m, 7x80k}; the first is the headline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm-cache", action="store_true", help="reuse one input copy (cache-resident)")
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="after timing, copy this many MiB device-to-device (counter calibration)")
+    ap.add_argument("--sweep", default="",
+                    help="comma list from {c1..c5, cp8_7x125k}: one JSON line per workload")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: rows are independent, so the path shards by rows with no "
               "exchange; multi-GPU runs are not part of this build (use --gpus 1).", file=sys.stderr)
         return 2
+    if args.sweep:
+        return sweep(args)
 
-    import numpy as np
     import oracle
-    import synth
 
-    w = synth.make_config(3)
-    w80 = synth.make_config(2)
-    res = measure(w, args.steps, args.warmup, rotate=not args.warm_cache)
-    res80 = measure(w80, args.steps, args.warmup, rotate=not args.warm_cache)
+    names = args.workloads.split(",")
+    for n in names:
+        if n not in DESCRIPTIONS:
+            ap.error(f"unknown workload {n}")
+    results = {}
+    for n in names:
+        w = workload(n)
+        say(f"[bench] {n}: {args.warmup} warmup + {args.steps} timed steps")
+        results[n] = (w, measure(w, args.steps, args.warmup, rotate=not args.warm_cache))
+    if args.calibrate_copy_mb:
+        calibrate_copy(args.calibrate_copy_mb)
 
+    head = names[0]
+    w, res = results[head]
     base = None
     if not args.no_cpu_baseline:
+        say(f"[bench] oracle CPU baseline on {head} for ~{args.cpu_seconds:g} s")
         base, ref = cpu_baseline(w, args.cpu_seconds)
     else:
         ref = oracle.topk_workload(w, threads=min(w.rows, os.cpu_count() or 1))
-    got = oracle.canonical(*res["out"])
-    want = oracle.canonical(*ref)
-    parity = bool(res["last_copy_equal"] and np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1]))
-    ref80 = oracle.canonical(*oracle.topk_workload(w80, threads=7))
-    got80 = oracle.canonical(*res80["out"])
-    parity80 = bool(np.array_equal(got80[0], ref80[0]) and np.array_equal(got80[1], ref80[1]))
+    parity = matches(res["out"], ref) and res["last_copy_equal"]
 
     nbytes = algorithmic_bytes(w, res["out"][1], True)
     achieved = nbytes / (res["select_ms"] * 1e-3) / 1e9
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        t = json.load(open(TRAFFIC_FILE))
+    if head == "7x1m" and os.path.exists(TRAFFIC_FILE):
+        t = json.loads(open(TRAFFIC_FILE).read())
         if t.get("kernel_source_sha") == kernel_source_digest():
             traffic = t.get("bytes_per_launch")
     step_us = res["ms_per_step"] * 1e3
@@ -189,12 +310,11 @@ def main() -> int:
         "ms_per_step": round(res["ms_per_step"], 6),
         "higher_is_better": False,
         "scaling": "weak",
-        "vs_baseline": round(step_us / PAGES_V2_1M_US, 4),
+        "vs_baseline": round(step_us / PAGES_V2_US[head], 4),
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": "7x1M k=2048: 7 rows x 1,000,000 FP32 scores ~N(0,1), 1% in [3.0,3.0005), "
-                        "64-token pages, shared random page permutation",
+            "workload": DESCRIPTIONS[head],
             "rows": w.rows, "row_len": w.stride, "k": w.k, "page_size": w.page_size,
             "cache": "warm (one input copy)" if args.warm_cache else
                      f"cold: {res['copies']} rotated input copies (>= 512 MB)",
@@ -213,18 +333,24 @@ def main() -> int:
         },
         "cpu_baseline": base,
         "select_us": {"mean": round(res["select_ms"] * 1e3, 3), "p10": round(res["select_p10_ms"] * 1e3, 3),
-                      "p50": round(res["select_p50_ms"] * 1e3, 3), "p90": round(res["select_p90_ms"] * 1e3, 3)},
+                      "p50": round(res["select_p50_ms"] * 1e3, 3), "p90": round(res["select_p90_ms"] * 1e3, 3),
+                      "stream_events_mean": round(res["select_stream_ms"] * 1e3, 3)},
         "plan_us": round(res["plan_ms"] * 1e3, 3),
-        "latency_7x80k_us": {"step": round(res80["ms_per_step"] * 1e3, 3),
-                             "select_mean": round(res80["select_ms"] * 1e3, 3),
-                             "select_p50": round(res80["select_p50_ms"] * 1e3, 3),
-                             "plan": round(res80["plan_ms"] * 1e3, 3),
-                             "parity": parity80},
         "parity": parity,
-        "pages_b300_context_us": {"topk_v2_80k": 17.5, "topk_v2_1m": 36.6},
+        "pages_b300_context_us": {"topk_v2_80k": PAGES_V2_US["7x80k"], "topk_v2_1m": PAGES_V2_US["7x1m"]},
     }
+    ok = parity
+    for n in names[1:]:
+        w2, r2 = results[n]
+        p2 = matches(r2["out"], oracle.topk_workload(w2, threads=min(w2.rows, os.cpu_count() or 1)))
+        ok &= p2
+        line[f"latency_{n}_us"] = {"step": round(r2["ms_per_step"] * 1e3, 3),
+                                   "select_mean": round(r2["select_ms"] * 1e3, 3),
+                                   "select_stream_events_mean": round(r2["select_stream_ms"] * 1e3, 3),
+                                   "select_p50": round(r2["select_p50_ms"] * 1e3, 3),
+                                   "plan": round(r2["plan_ms"] * 1e3, 3), "parity": p2}
     print(json.dumps(line), flush=True)
-    return 0 if (parity and parity80) else 1
+    return 0 if ok else 1
 
 
 if __name__ == "__main__":

@@ -136,6 +136,22 @@ topk_status topk_select_paged(const topk_config* cfg, const void* plan,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * topk_select_paged for measurement: identical arguments, results and errors,
+ * plus two HIP events (hipEvent_t, created by the caller, timing enabled)
+ * that record the selection kernel's own start and end, as a kernel trace
+ * reports them, rather than the stream position before and after it.
+ * Both events are required (INVALID_ARG otherwise).
+ */
+topk_status topk_select_paged_timed(const topk_config* cfg, const void* plan,
+                                    const float* scores, int64_t score_row_stride,
+                                    const int32_t* lengths, int32_t num_rows,
+                                    const int32_t* block_table, int64_t bt_row_stride,
+                                    int32_t page_size,
+                                    int32_t* out_slots, int32_t* out_indices, int64_t out_row_stride,
+                                    void* workspace, size_t workspace_bytes, void* stream,
+                                    void* start_event, void* stop_event);
+
+/*
  * SYNCHRONISES `stream`. Copies the device status word of `workspace` into
  * *host_status (host pointer): 0, or a bitwise OR of TOPK_DEVICE_* flags.
  * Returns TOPK_ERR_DEVICE when the word is non-zero.

@@ -10,7 +10,7 @@
 
 namespace satopk {
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
-hipError_t launch_select(const SelectArgs& a, int grid, bool vec, hipStream_t s);
+hipError_t launch_select(const SelectArgs& a, int grid, bool vec, hipStream_t s, hipEvent_t start, hipEvent_t stop);
 hipError_t launch_fill(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_debug_keys(const float* x, int64_t n, uint32_t* bin, uint32_t* k32, hipStream_t s);
 hipError_t select_occupancy(int* per_cu);
@@ -137,11 +137,15 @@ topk_status topk_plan(const topk_config* cfg, const int32_t* lengths, int32_t nu
   return launch_plan(a, (hipStream_t)stream) == hipSuccess ? TOPK_OK : TOPK_ERR_HIP;
 }
 
-topk_status topk_select_paged(const topk_config* cfg, const void* plan, const float* scores,
-                              int64_t score_row_stride, const int32_t* lengths, int32_t num_rows,
-                              const int32_t* block_table, int64_t bt_row_stride, int32_t page_size,
-                              int32_t* out_slots, int32_t* out_indices, int64_t out_row_stride, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+topk_status select_impl(const topk_config* cfg, const void* plan, const float* scores, int64_t score_row_stride,
+                        const int32_t* lengths, int32_t num_rows, const int32_t* block_table, int64_t bt_row_stride,
+                        int32_t page_size, int32_t* out_slots, int32_t* out_indices, int64_t out_row_stride,
+                        void* workspace, size_t workspace_bytes, void* stream, void* start_event,
+                        void* stop_event) {
   Sizing s;
   const topk_status st = sizing(cfg, &s);
   if (st != TOPK_OK) return st;
@@ -179,7 +183,35 @@ topk_status topk_select_paged(const topk_config* cfg, const void* plan, const fl
   a.max_len = cfg->max_len;
   a.spin_limit = kDefaultSpinLimit;
   const bool vec = ((uintptr_t)scores % 16 == 0) && (score_row_stride % 4 == 0);
-  return launch_select(a, s.grid, vec, (hipStream_t)stream) == hipSuccess ? TOPK_OK : TOPK_ERR_HIP;
+  return launch_select(a, s.grid, vec, (hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event) ==
+                 hipSuccess
+             ? TOPK_OK
+             : TOPK_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+topk_status topk_select_paged(const topk_config* cfg, const void* plan, const float* scores,
+                              int64_t score_row_stride, const int32_t* lengths, int32_t num_rows,
+                              const int32_t* block_table, int64_t bt_row_stride, int32_t page_size,
+                              int32_t* out_slots, int32_t* out_indices, int64_t out_row_stride, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return select_impl(cfg, plan, scores, score_row_stride, lengths, num_rows, block_table, bt_row_stride, page_size,
+                     out_slots, out_indices, out_row_stride, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+topk_status topk_select_paged_timed(const topk_config* cfg, const void* plan, const float* scores,
+                                    int64_t score_row_stride, const int32_t* lengths, int32_t num_rows,
+                                    const int32_t* block_table, int64_t bt_row_stride, int32_t page_size,
+                                    int32_t* out_slots, int32_t* out_indices, int64_t out_row_stride,
+                                    void* workspace, size_t workspace_bytes, void* stream, void* start_event,
+                                    void* stop_event) {
+  if (!start_event || !stop_event) return TOPK_ERR_INVALID_ARG;
+  return select_impl(cfg, plan, scores, score_row_stride, lengths, num_rows, block_table, bt_row_stride, page_size,
+                     out_slots, out_indices, out_row_stride, workspace, workspace_bytes, stream, start_event,
+                     stop_event);
 }
 
 topk_status topk_read_status(const void* workspace, size_t workspace_bytes, int32_t* host_status, void* stream) {

@@ -20,6 +20,7 @@
 // above their own local k-th bin, since the row's k-th score can never lie
 // below any chunk's k-th score.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include "sparse_topk.h"
 #include "topk_device.hpp"
@@ -1235,9 +1236,17 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_select(const SelectArgs& a, int grid, bool vec, hipStream_t s) {
-  if (vec) hipLaunchKernelGGL(topk_select_kernel<true>, dim3(grid), dim3(kBlock), 0, s, a);
-  else hipLaunchKernelGGL(topk_select_kernel<false>, dim3(grid), dim3(kBlock), 0, s, a);
+// With events, they record the dispatch's own start and end (the same
+// interval a kernel trace reports), not the stream position around it.
+hipError_t launch_select(const SelectArgs& a, int grid, bool vec, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+  if (start || stop) {
+    if (vec) hipExtLaunchKernelGGL(topk_select_kernel<true>, dim3(grid), dim3(kBlock), 0, s, start, stop, 0, a);
+    else hipExtLaunchKernelGGL(topk_select_kernel<false>, dim3(grid), dim3(kBlock), 0, s, start, stop, 0, a);
+  } else if (vec) {
+    hipLaunchKernelGGL(topk_select_kernel<true>, dim3(grid), dim3(kBlock), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(topk_select_kernel<false>, dim3(grid), dim3(kBlock), 0, s, a);
+  }
   return hipGetLastError();
 }
 

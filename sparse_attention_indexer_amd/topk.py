@@ -60,6 +60,7 @@ def load_library():
         "topk_workspace_init": [V, S, V],
         "topk_plan": [P, V, I32, V, S, V],
         "topk_select_paged": [P, V, V, I64, V, I32, V, I64, I32, V, V, I64, V, S, V],
+        "topk_select_paged_timed": [P, V, V, I64, V, I32, V, I64, I32, V, V, I64, V, S, V, V, V],
         "topk_read_status": [V, S, ctypes.POINTER(I32), V],
         "topk_debug_keys": [V, I64, V, V, V],
     }
@@ -125,10 +126,8 @@ def topk_plan(cfg: topk_config, lengths: torch.Tensor, plan: torch.Tensor, strea
         plan.numel() * plan.element_size(), _stream(stream)))
 
 
-def topk_select_paged(cfg: topk_config, plan: torch.Tensor, scores: torch.Tensor, lengths: torch.Tensor,
-                      block_table: torch.Tensor, bt_row_stride: int, page_size: int,
-                      out_slots: torch.Tensor, out_indices: torch.Tensor | None,
-                      workspace: torch.Tensor, stream=None) -> None:
+def _select_args(cfg, plan, scores, lengths, block_table, bt_row_stride, page_size, out_slots, out_indices,
+                 workspace, stream):
     _need(scores, torch.float32, "scores")
     _need(lengths, torch.int32, "lengths")
     _need(block_table, torch.int32, "block_table")
@@ -144,11 +143,39 @@ def topk_select_paged(cfg: topk_config, plan: torch.Tensor, scores: torch.Tensor
     rows = lengths.numel()
     if scores.shape[0] < rows or out_slots.shape[0] < rows:
         raise ValueError("scores and out_slots need a row per length")
-    _check("topk_select_paged", load_library().topk_select_paged(
-        ctypes.byref(cfg), plan.data_ptr(), scores.data_ptr(), scores.stride(0), lengths.data_ptr(), rows,
-        block_table.data_ptr(), int(bt_row_stride), int(page_size), out_slots.data_ptr(),
-        _ptr(out_indices), out_slots.stride(0), workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return (ctypes.byref(cfg), plan.data_ptr(), scores.data_ptr(), scores.stride(0), lengths.data_ptr(), rows,
+            block_table.data_ptr(), int(bt_row_stride), int(page_size), out_slots.data_ptr(),
+            _ptr(out_indices), out_slots.stride(0), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def topk_select_paged(cfg: topk_config, plan: torch.Tensor, scores: torch.Tensor, lengths: torch.Tensor,
+                      block_table: torch.Tensor, bt_row_stride: int, page_size: int,
+                      out_slots: torch.Tensor, out_indices: torch.Tensor | None,
+                      workspace: torch.Tensor, stream=None) -> None:
+    args = _select_args(cfg, plan, scores, lengths, block_table, bt_row_stride, page_size, out_slots,
+                        out_indices, workspace, stream)
+    _check("topk_select_paged", load_library().topk_select_paged(*args))
+
+
+def _event_handle(ev: "torch.cuda.Event") -> int:
+    """The hipEvent_t behind a torch event (torch creates it on first record)."""
+    if not ev.cuda_event:
+        ev.record()
+    return int(ev.cuda_event)
+
+
+def topk_select_paged_timed(cfg: topk_config, plan: torch.Tensor, scores: torch.Tensor, lengths: torch.Tensor,
+                            block_table: torch.Tensor, bt_row_stride: int, page_size: int,
+                            out_slots: torch.Tensor, out_indices: torch.Tensor | None,
+                            workspace: torch.Tensor, start: "torch.cuda.Event", stop: "torch.cuda.Event",
+                            stream=None) -> None:
+    """topk_select_paged whose kernel records its own start and end into two
+    timing-enabled torch events (read them with start.elapsed_time(stop))."""
+    args = _select_args(cfg, plan, scores, lengths, block_table, bt_row_stride, page_size, out_slots,
+                        out_indices, workspace, stream)
+    _check("topk_select_paged_timed", load_library().topk_select_paged_timed(
+        *args, _event_handle(start), _event_handle(stop)))
 
 
 def topk_read_status(workspace: torch.Tensor, stream=None) -> int:
@@ -195,14 +222,20 @@ class TopK:
 
     def select(self, scores: torch.Tensor, lengths: torch.Tensor, block_table: torch.Tensor,
                bt_row_stride: int, page_size: int, *, out_slots: torch.Tensor | None = None,
-               out_indices: torch.Tensor | None = None, with_indices: bool = True, stream=None):
+               out_indices: torch.Tensor | None = None, with_indices: bool = True, stream=None,
+               events: tuple | None = None):
         rows = lengths.numel()
         if out_slots is None:
             out_slots = torch.empty((rows, self.k), dtype=torch.int32, device=scores.device)
         if out_indices is None and with_indices:
             out_indices = torch.empty_like(out_slots)
-        topk_select_paged(self.cfg, self.plan_buf, scores, lengths, block_table, bt_row_stride, page_size,
-                          out_slots, out_indices, self.workspace, stream)
+        if events is None:
+            topk_select_paged(self.cfg, self.plan_buf, scores, lengths, block_table, bt_row_stride, page_size,
+                              out_slots, out_indices, self.workspace, stream)
+        else:
+            topk_select_paged_timed(self.cfg, self.plan_buf, scores, lengths, block_table, bt_row_stride,
+                                    page_size, out_slots, out_indices, self.workspace, events[0], events[1],
+                                    stream)
         return out_slots, out_indices
 
     def status(self, stream=None) -> int:

@@ -28,7 +28,8 @@ def T():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("topk_query_sizes", "topk_plan", "topk_select_paged", "topk_workspace_init",
-              "topk_read_status", "topk_status_string", "topk_register_capacity", "topk_debug_keys"):
+              "topk_read_status", "topk_status_string", "topk_register_capacity", "topk_debug_keys",
+              "topk_select_paged_timed"):
         assert n in names
 
 
@@ -91,6 +92,9 @@ def test_null_arguments_rejected(T):
     assert lib.topk_plan(ctypes.byref(bad), None, 7, None, 0, None) == T.TOPK_ERR_INVALID_ARG
     assert lib.topk_select_paged(ctypes.byref(bad), None, None, 0, None, 7, None, 0, 64,
                                  None, None, 2048, None, 0, None) == T.TOPK_ERR_INVALID_ARG
+    good = T.make_config(2048, 7, 80_000)
+    assert lib.topk_select_paged_timed(ctypes.byref(good), None, None, 0, None, 7, None, 0, 64,
+                                       None, None, 2048, None, 0, None, None, None) == T.TOPK_ERR_INVALID_ARG
 
 
 def test_valid_config_needs_a_device(T):

@@ -191,3 +191,30 @@ def test_many_ragged_rows(rows, prefix, k):
     w = synth.Workload(f"ragged{rows}", np.ascontiguousarray(scores), lengths, bt, 0, 64, k, 1)
     _gpu.say(f"[ragged] rows {rows} prefix {prefix} k {k}")
     _gpu.assert_matches_oracle(w, _gpu.run_gpu(w, "auto"), f"ragged {rows}")
+
+
+def test_timed_entry_matches_and_times_the_kernel(workloads):
+    """topk_select_paged_timed gives the untimed call's result, and its kernel
+    events bracket a positive interval no longer than the stream's view."""
+    from sparse_attention_indexer_amd import topk
+    w = workloads[2]
+    dev = torch.device("cuda:0")
+    tk = topk.TopK(w.k, w.rows, w.max_len, device=dev)
+    sc = torch.from_numpy(w.scores).to(dev)
+    ln = torch.from_numpy(w.lengths).to(dev)
+    bt = torch.from_numpy(np.ascontiguousarray(w.block_table)).to(dev)
+    tk.plan(ln)
+    s0, i0 = tk.select(sc, ln, bt, w.bt_row_stride, w.page_size)
+    ks, ke, ss, se = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+    ss.record()
+    s1, i1 = tk.select(sc, ln, bt, w.bt_row_stride, w.page_size, events=(ks, ke))
+    se.record()
+    torch.cuda.synchronize()
+    assert tk.status() == 0
+    # the order within a row is unspecified: compare each row's sorted entries
+    assert torch.equal(s0.sort(dim=1).values, s1.sort(dim=1).values)
+    assert torch.equal(i0.sort(dim=1).values, i1.sort(dim=1).values)
+    _gpu.assert_matches_oracle(w, (i1.cpu().numpy(), s1.cpu().numpy()), "timed")
+    kernel_ms, stream_ms = ks.elapsed_time(ke), ss.elapsed_time(se)
+    _gpu.say(f"[timed] kernel {kernel_ms * 1e3:.1f} us, stream {stream_ms * 1e3:.1f} us")
+    assert 0 < kernel_ms <= stream_ms * 1.01
