@@ -138,20 +138,28 @@ __device__ __forceinline__ void find_threshold(const uint32_t* hist, int nb, uin
     const int b = nb - 1 - (t * PB + j);
     s += b >= 0 ? hist[bin_addr<PB, PAD>(b)] : 0u;
   }
-  uint32_t cum = block_exclusive_add(s, scratch);
-  // Only the thread whose bins straddle `need` re-reads them (cheap LDS reads
-  // instead of PB registers held across the scan).
-  if (cum < need && need <= cum + s) {
-    for (int j = 0; j < PB; ++j) {
-      const int b = nb - 1 - (t * PB + j);
-      const uint32_t h = b >= 0 ? hist[bin_addr<PB, PAD>(b)] : 0u;
-      if (cum < need && need <= cum + h) {
-        result[0] = (uint32_t)b;
-        result[1] = cum;
-        result[2] = h;
-        break;
-      }
-      cum += h;
+  const uint32_t cum = block_exclusive_add(s, scratch);
+  // The wave holding the thread whose bins straddle `need` resolves them in
+  // parallel: lane l < PB takes that thread's l-th bin, and a 16-lane DPP
+  // prefix sum replaces a serial rescan of dependent LDS reads.
+  static_assert(PB <= 16, "one DPP row holds the straddling thread's bins");
+  const uint64_t strad = __ballot(cum < need && need <= cum + s);
+  if (strad) {
+    const uint32_t sl = first_lane(strad);
+    const uint32_t c0 = read_lane(cum, sl);
+    const int ts = (t & ~63) + (int)sl;
+    const int l = (int)lane();
+    const int b = nb - 1 - (ts * PB + l);
+    const uint32_t h = (l < PB && b >= 0) ? hist[bin_addr<PB, PAD>(b)] : 0u;
+    uint32_t inc = h;
+    inc += SATOPK_DPP(inc, 0x111, 0xf);  // row_shr:1
+    inc += SATOPK_DPP(inc, 0x112, 0xf);  // row_shr:2
+    inc += SATOPK_DPP(inc, 0x114, 0xf);  // row_shr:4
+    inc += SATOPK_DPP(inc, 0x118, 0xf);  // row_shr:8
+    if (l < PB && c0 + inc - h < need && need <= c0 + inc) {
+      result[0] = (uint32_t)b;
+      result[1] = c0 + inc - h;
+      result[2] = h;
     }
   }
   __syncthreads();

@@ -760,31 +760,44 @@ __device__ __forceinline__ void refine(const Src& src, const Refine& p, Smem& sh
 template <int J>
 __device__ __forceinline__ void resolve_regs(const uint32_t (&kd)[J], const uint32_t (&ps)[J], uint32_t n,
                                              const Refine& p, Smem& sh, const RowOut& o) {
+  static_assert(J * kBlock + 2 * kBlock <= kListCap, "per-lane sink slots lie past the candidates");
+  static_assert((kWideWords + kBlock) / 2 <= kListCap - 2 * kBlock, "histogram sinks precede the write sinks");
   const int t = threadIdx.x;
   const bool wide = n > 4096u;
-  const uint32_t b1 = p.nb - p.b2;
   const uint32_t width = min(wide ? (uint32_t)kFirstRadixBits : (uint32_t)kRadixBits, p.nb);
   const uint32_t shift = p.nb - width;
   const uint32_t mask = (1u << width) - 1u;
   const uint32_t pad = wide ? 4u : 2u;   // log2 of the bins each lane scans
-  const bool key_only = b1 >= width;     // digit = kd >> (b1 - width)
   // lane t holds nv valid entries: j * kBlock + t < n  <=>  j < nv
   const int nv = (int)((n + kBlock - 1 - (uint32_t)t) / kBlock);
+  // Top `width` bits of the composite key (one formula whether or not they
+  // reach into the position bits).
+  // In 32-bit arithmetic: when the digit lies inside the key bits (shift >=
+  // b2) it is kd >> (shift - b2); otherwise kd's bits shifted up by b2 - shift
+  // join the top bits of the reversed position.
+  const bool key_only = shift >= p.b2;
+  const uint32_t sl = key_only ? 0u : p.b2 - shift;
+  const uint32_t sr = key_only ? shift - p.b2 : 0u;
+  const uint32_t rs = key_only ? 0u : shift;
+  const uint32_t rm = key_only ? 0u : 0xFFFFFFFFu;
+  // (Recomputed in each loop rather than held: an empty asm hides the value
+  // from common-subexpression elimination, which would keep J digits live.)
   auto digit = [&](int j) -> uint32_t {
-    if (key_only) return kd[j] >> (b1 - width);
-    const uint64_t ck = ((uint64_t)kd[j] << p.b2) | (uint64_t)(p.idx_hi - ps[j]);
-    return (uint32_t)(ck >> shift) & mask;
+    uint32_t x = kd[j];
+    asm volatile("" : "+v"(x));
+    return (((x << sl) >> sr) | (((p.idx_hi - ps[j]) >> rs) & rm)) & mask;
   };
   uint32_t* hist = reinterpret_cast<uint32_t*>(sh.list);
   const uint32_t words = (mask + 1) + ((mask + 1) >> pad);
   for (int i = t; i < (int)words; i += kBlock) hist[i] = 0;
   __syncthreads();
+  // Invalid slots add into this lane's own sink word past the histogram (one
+  // shared sink would serialise whole waves on a single address).
+  const uint32_t sink = words + (uint32_t)t;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    if (j < nv) {
-      const uint32_t d = digit(j);
-      atomicAdd(&hist[d + (d >> pad)], 1u);
-    }
+    const uint32_t d = digit(j);
+    atomicAdd(&hist[j < nv ? d + (d >> pad) : sink], 1u);
   }
   __syncthreads();
   if (t == 0) sh.res[0] = kNotFound;
@@ -796,33 +809,43 @@ __device__ __forceinline__ void resolve_regs(const uint32_t (&kd)[J], const uint
     return;
   }
   const bool finish = cnt == p.need - above;
-  const uint32_t dlo = finish ? d : d + 1;   // emitted: digit >= dlo; kept: digit == d (unless finish)
+  const uint32_t dlo = finish ? d : d + 1;   // emitted: digit >= dlo; kept (unless finish): digit == d
+  const uint32_t dkeep = finish ? 0xFFFFFFFFu : d;
   uint32_t na = 0, nk = 0;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const uint32_t dj = digit(j);
     na += (j < nv && dj >= dlo) ? 1u : 0u;
-    nk += (j < nv && dj == d) ? 1u : 0u;
+    nk += (j < nv && dj == dkeep) ? 1u : 0u;
   }
-  if (finish) nk = 0;
   const uint32_t base = uni(sh.cur_out);
   uint32_t tot;
   const uint32_t off = block_exclusive_add((nk << 16) | na, sh.scratch, &tot);   // counts < 2^16
-  uint32_t ao = base + (off & 0xFFFFu), ko = off >> 16;
-  bool bad = false;
-  if (na | nk) {
+  const uint32_t total_out = tot & 0xFFFFu, total_keep = tot >> 16;
+  // The counts bound every write, so one uniform check replaces per-element
+  // bounds checks; unselected slots write to this lane's own sink entries past
+  // the candidates (no branches, no bank conflicts among the sinks).
+  const bool ok = base + total_out <= o.k && total_keep <= (uint32_t)(kListCap - 2 * kBlock);
+  if (ok) {
+    uint32_t* stage_sink = reinterpret_cast<uint32_t*>(sh.list + (kListCap - 2 * kBlock)) + t;
+    uint64_t* list_sink = sh.list + (kListCap - kBlock) + t;
+    uint32_t ao = base + (off & 0xFFFFu), ko = off >> 16;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const uint32_t dj = digit(j);
-      if (j < nv && dj >= dlo) bad |= !o.write(ao++, (int32_t)ps[j]);
-      if (!finish && j < nv && dj == d) sh.list[ko++] = p.key(kd[j] + p.lo32, (int32_t)ps[j]);
+      const bool em = j < nv && dj >= dlo;
+      const bool kp = j < nv && dj == dkeep;
+      *(em ? sh.outpos + ao : stage_sink) = ps[j];   // o.stage is sh.outpos
+      *(kp ? sh.list + ko : list_sink) = p.key(kd[j] + p.lo32, (int32_t)ps[j]);
+      ao += em ? 1u : 0u;
+      ko += kp ? 1u : 0u;
     }
   }
-  report_bad(bad, o.status);
+  report_bad(!ok, o.status);
   __syncthreads();
-  if (t == 0) sh.cur_out = base + (tot & 0xFFFFu);
+  if (t == 0) sh.cur_out = base + total_out;
   __syncthreads();
-  if (finish) return;
+  if (finish || !ok) return;
   refine<true>(KeyListSrc{sh.list, cnt}, p, sh, o, (uint64_t)d, width, p.need - above, cnt);
 }
 
@@ -1055,13 +1078,17 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
   const bool stage = keep && local_cnt <= (uint32_t)kListCap;   // candidates staged in LDS
   // This workgroup's output and candidate offsets in the row; their round
   // trips overlap the re-reads of the extraction below.
+  // (Only the rare unstaged case, candidates written straight to global
+  // memory, needs its base before the extraction; otherwise thread 0 reads
+  // the atomics' results after it.)
   uint32_t base_out = 0, base_cand = 0;
   if (t == 0) {
     if (local_above) base_out = __hip_atomic_fetch_add(&g->emit, local_above, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (keep && local_cnt) base_cand = __hip_atomic_fetch_add(&g->cand, local_cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sh.cur_out = 0;
-    sh.cur_list = (keep && !stage) ? base_cand : 0u;
     sh.range[0] = sh.range[1] = sh.range[2] = sh.range[3] = 0;
+    if (keep && !stage) sh.cur_list = base_cand;
+    else sh.cur_list = 0u;
   }
   __syncthreads();
   uint64_t* slab = a.cand + (int64_t)w.group * a.cand_cap;
