@@ -32,6 +32,7 @@ METRIC = "TopK latency (µs) at 7×80K and 7×1M, k=2048; HBM GB/s vs peak"
 PEAK_HBM_GBS = 8000.0
 PAGES_V2_US = {"7x1m": 36.6, "7x80k": 17.5}   # the page's TopK-V2 latencies (B300; context only)
 ROTATION_BYTES = 512 << 20
+IN_KERNEL_PLAN_ROWS = 512      # batches this small are planned inside topk_select_paged
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "topk_select_kernel_7x1m_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "sparse_attention_indexer_amd", "csrc", f)
                   for f in ("topk_kernels.hip", "topk_device.hpp", "topk_layout.hpp")]
@@ -234,7 +235,8 @@ def sweep(args) -> int:
             "workload": w.name, "rows": w.rows, "stride": w.stride, "k": w.k,
             "select_us": {"p50": round(res["select_p50_ms"] * 1e3, 3), "p10": round(res["select_p10_ms"] * 1e3, 3),
                           "p90": round(res["select_p90_ms"] * 1e3, 3), "mean": round(res["select_ms"] * 1e3, 3)},
-            "plan_us": round(res["plan_ms"] * 1e3, 3), "step_us": round(res["ms_per_step"] * 1e3, 3),
+            "plan_us": round(res["plan_ms"] * 1e3, 3) if w.rows > IN_KERNEL_PLAN_ROWS else "in-kernel",
+            "step_us": round(res["ms_per_step"] * 1e3, 3),
             "rows_per_s": round(w.rows / p50), "algorithmic_bytes": nbytes,
             "gbs": round(nbytes / p50 / 1e9, 1), "frac_of_8tbs": round(nbytes / p50 / 1e9 / PEAK_HBM_GBS, 4),
             "cache": "warm" if args.warm_cache else f"cold ({res['copies']} copies)",
@@ -335,7 +337,8 @@ def main() -> int:
         "select_us": {"mean": round(res["select_ms"] * 1e3, 3), "p10": round(res["select_p10_ms"] * 1e3, 3),
                       "p50": round(res["select_p50_ms"] * 1e3, 3), "p90": round(res["select_p90_ms"] * 1e3, 3),
                       "stream_events_mean": round(res["select_stream_ms"] * 1e3, 3)},
-        "plan_us": round(res["plan_ms"] * 1e3, 3),
+        "plan_us": round(res["plan_ms"] * 1e3, 3) if w.rows > IN_KERNEL_PLAN_ROWS else None,
+        "plan": "in the selection kernel" if w.rows <= IN_KERNEL_PLAN_ROWS else "topk_plan kernel",
         "parity": parity,
         "pages_b300_context_us": {"topk_v2_80k": PAGES_V2_US["7x80k"], "topk_v2_1m": PAGES_V2_US["7x1m"]},
     }
@@ -348,7 +351,8 @@ def main() -> int:
                                    "select_mean": round(r2["select_ms"] * 1e3, 3),
                                    "select_stream_events_mean": round(r2["select_stream_ms"] * 1e3, 3),
                                    "select_p50": round(r2["select_p50_ms"] * 1e3, 3),
-                                   "plan": round(r2["plan_ms"] * 1e3, 3), "parity": p2}
+                                   "plan": round(r2["plan_ms"] * 1e3, 3) if w2.rows > IN_KERNEL_PLAN_ROWS
+                                   else "in the selection kernel", "parity": p2}
     print(json.dumps(line), flush=True)
     return 0 if ok else 1
 

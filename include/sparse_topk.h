@@ -109,8 +109,12 @@ topk_status topk_workspace_init(void* workspace, size_t workspace_bytes, void* s
  * device kernel reads `lengths` (int32[num_rows], device) and writes the work
  * list into `plan`. Run it once per forward; the plan stays valid for any
  * number of topk_select_paged calls whose lengths are the same values.
+ * Batches of at most TOPK_IN_KERNEL_PLAN_ROWS rows are planned inside the
+ * selection kernel instead (from the same lengths, with the same result), so
+ * for them this call checks its arguments and enqueues nothing.
  * 0 <= num_rows <= cfg->max_rows. No host synchronisation.
  */
+#define TOPK_IN_KERNEL_PLAN_ROWS 512
 topk_status topk_plan(const topk_config* cfg, const int32_t* lengths, int32_t num_rows,
                       void* plan, size_t plan_bytes, void* stream);
 
@@ -123,7 +127,8 @@ topk_status topk_plan(const topk_config* cfg, const int32_t* lengths, int32_t nu
  *   page_size       tokens per KV page, >= 1.
  *   out_slots       int32[num_rows][out_row_stride], out_row_stride >= k.
  *   out_indices     int32[num_rows][out_row_stride] or NULL.
- *   plan            written by topk_plan for the same cfg and lengths.
+ *   plan            written by topk_plan for the same cfg and lengths; not read
+ *                   (and may be NULL) when num_rows <= TOPK_IN_KERNEL_PLAN_ROWS.
  *   workspace       >= topk_query_sizes bytes, zeroed once by topk_workspace_init.
  * Status: OK, INVALID_ARG, BUFFER_TOO_SMALL, UNSUPPORTED, HIP. No host synchronisation.
  */

@@ -8,6 +8,9 @@
 #include "sparse_topk.h"
 #include "topk_layout.hpp"
 
+static_assert(satopk::kInKernelPlanRows == TOPK_IN_KERNEL_PLAN_ROWS, "header and kernels agree");
+static_assert(satopk::kInKernelPlanRows <= satopk::kBlock, "one row per thread");
+
 namespace satopk {
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, int grid, bool vec, hipStream_t s, hipEvent_t start, hipEvent_t stop);
@@ -70,15 +73,25 @@ topk_status sizing(const topk_config* cfg, Sizing* s) {
   DevInfo d;
   st = device_info(&d);
   if (st != TOPK_OK) return st;
-  s->grid = d.cus * d.per_cu;
+  // The persistent grid: every co-resident workgroup, but no more than the
+  // configuration can use (rows x chunks of a longest row), so small batches
+  // launch few workgroups.
+  const int64_t min_chunk = cfg->min_chunk > 0 ? cfg->min_chunk : kDefaultMinChunk;
+  int64_t per_row = (cfg->max_len + min_chunk - 1) / min_chunk;
+  if (cfg->force_path == TOPK_PATH_MULTI && per_row < 2) per_row = 2;
+  if (cfg->wg_per_row > per_row) per_row = cfg->wg_per_row;
+  if (per_row < 1) per_row = 1;
+  const int64_t want = (int64_t)cfg->max_rows * per_row;
+  const int64_t cap = (int64_t)d.cus * d.per_cu;
+  s->grid = (int)(want < cap ? want : cap);
   s->max_items = s->grid + cfg->max_rows;
   int groups = s->grid / 2;
   if (groups > cfg->max_rows) groups = cfg->max_rows;
   if (groups < 1) groups = 1;
   s->max_groups = groups;
-  int64_t cap = cfg->cand_capacity > 0 ? cfg->cand_capacity
-                                       : (cfg->max_len < kDefaultCandCap ? cfg->max_len : kDefaultCandCap);
-  s->cand_cap = cap < 1 ? 1 : cap;
+  const int64_t cand = cfg->cand_capacity > 0 ? cfg->cand_capacity
+                                             : (cfg->max_len < kDefaultCandCap ? cfg->max_len : kDefaultCandCap);
+  s->cand_cap = cand < 1 ? 1 : cand;
   const bool splits = cfg->force_path == TOPK_PATH_AUTO || cfg->force_path == TOPK_PATH_MULTI;
   // every row split needs its own group state and at least two workgroups of one grid round
   if (cfg->force_path == TOPK_PATH_MULTI && (int64_t)cfg->max_rows * 2 > s->grid) return TOPK_ERR_UNSUPPORTED;
@@ -119,7 +132,7 @@ topk_status topk_plan(const topk_config* cfg, const int32_t* lengths, int32_t nu
   if (num_rows < 0 || num_rows > cfg->max_rows || !plan) return TOPK_ERR_INVALID_ARG;
   if (num_rows > 0 && !lengths) return TOPK_ERR_INVALID_ARG;
   if (plan_bytes < s.plan_bytes) return TOPK_ERR_BUFFER_TOO_SMALL;
-  if (num_rows == 0) return TOPK_OK;
+  if (num_rows <= kInKernelPlanRows) return TOPK_OK;   // the selection kernel plans these itself
   const bool no_split = cfg->force_path == TOPK_PATH_REGISTER || cfg->force_path == TOPK_PATH_SINGLE;
   PlanArgs a;
   a.lengths = lengths;
@@ -152,7 +165,7 @@ topk_status select_impl(const topk_config* cfg, const void* plan, const float* s
   if (num_rows < 0 || num_rows > cfg->max_rows) return TOPK_ERR_INVALID_ARG;
   if (page_size < 1 || bt_row_stride < 0 || out_row_stride < cfg->k) return TOPK_ERR_INVALID_ARG;
   if (score_row_stride < cfg->max_len || score_row_stride < 0) return TOPK_ERR_INVALID_ARG;
-  if (!plan || !workspace) return TOPK_ERR_INVALID_ARG;
+  if ((!plan && num_rows > kInKernelPlanRows) || !workspace) return TOPK_ERR_INVALID_ARG;
   if (num_rows > 0 && (!scores || !lengths || !block_table || !out_slots)) return TOPK_ERR_INVALID_ARG;
   if (workspace_bytes < s.workspace_bytes) return TOPK_ERR_BUFFER_TOO_SMALL;
   if (num_rows == 0) return TOPK_OK;
@@ -174,8 +187,13 @@ topk_status select_impl(const topk_config* cfg, const void* plan, const float* s
   a.out_slots = out_slots;
   a.out_idx = out_indices;
   a.out_stride = out_row_stride;
-  a.plan = (const PlanHeader*)plan;
-  a.items = (const WorkItem*)((const char*)plan + sizeof(PlanHeader));
+  const bool here = num_rows <= kInKernelPlanRows;
+  a.plan = here ? nullptr : (const PlanHeader*)plan;
+  a.items = here ? nullptr : (const WorkItem*)((const char*)plan + sizeof(PlanHeader));
+  a.force_path = cfg->force_path;
+  a.wg_per_row = (cfg->force_path == TOPK_PATH_REGISTER || cfg->force_path == TOPK_PATH_SINGLE) ? 0 : cfg->wg_per_row;
+  a.min_chunk = cfg->min_chunk;
+  a.max_groups = s.max_groups;
   a.groups = (GroupState*)((char*)workspace + ws_group_offset());
   a.cand = (uint64_t*)((char*)workspace + ws_cand_offset(s));
   a.cand_cap = s.cand_cap;

@@ -272,6 +272,10 @@ constexpr int kResolveRegs = 24;                    // candidates per lane of th
 static_assert(kWideWords * 4 <= kListCap * 8, "first-digit histogram aliases the LDS list");
 static_assert(kMaxK <= kRadixBins, "above-threshold staging aliases rhist");
 
+// Items one workgroup takes from an in-kernel plan: at most one split item
+// (split rows fit one grid round) plus ceil(rows / grid) whole rows.
+constexpr int kMaxLocalItems = 16;
+
 struct __align__(16) Smem {
   uint64_t list[kListCap];      // boundary candidates: (key32 << 32 | position), then composite keys
   uint32_t lhist[kBins];        // this workgroup's histogram (raw index)
@@ -284,6 +288,8 @@ struct __align__(16) Smem {
   uint32_t flag;
   uint32_t range[4];            // candidate key/position range: kmax, ~kmin, imax, ~imin
   uint32_t bcast[4];
+  uint64_t pl_red[kWaves];
+  WorkItem pl_items[kMaxLocalItems];   // in-kernel plan: this workgroup's items, in loop order
 };
 
 // Output of one row: slot = table[i / ps] * ps + i % ps (page: TopK-V2,
@@ -1223,20 +1229,116 @@ __device__ __forceinline__ void process_item(const SelectArgs& a, const WorkItem
   else split_row<VEC>(a, w, len, rowp, o, resident, hk, sh);
 }
 
+// In-kernel planning for small batches: thread t holds row t. Every
+// workgroup computes the same split counts and item offsets as
+// topk_plan_kernel (the same split_of) and writes the items that fall to it
+// (item it goes to workgroup it % grid, as in the plan-buffer loop) into LDS.
+// Returns the number of items, or -1 if the plan would not fit.
+
+__device__ __forceinline__ PlanArgs plan_args_of(const SelectArgs& a) {
+  PlanArgs p;
+  p.lengths = a.lengths;
+  p.num_rows = a.num_rows;
+  p.k = a.k;
+  p.grid = (int32_t)gridDim.x;
+  p.max_groups = a.max_groups;
+  p.max_items = 0;
+  p.force_path = a.force_path;
+  p.wg_per_row = a.wg_per_row;
+  p.min_chunk = a.min_chunk;
+  p.max_len = a.max_len;
+  p.header = nullptr;
+  p.items = nullptr;
+  return p;
+}
+
+__device__ __forceinline__ int plan_here(const SelectArgs& a, Smem& sh) {
+  const int t = threadIdx.x;
+  const int R = a.num_rows;
+  const int32_t len = t < R ? a.lengths[t] : 0;
+  const bool longer = t < R && len > a.k;
+  uint64_t mine = longer ? (uint64_t)len + (1ull << 40) : 0ull;   // lengths < 2^31, rows < 2^23
+  mine = wave_sum_u64(mine);
+  if (lane() == 0) sh.pl_red[t >> 6] = mine;
+  __syncthreads();
+  uint64_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) packed += sh.pl_red[i];
+  const uint64_t total = packed & ((1ull << 40) - 1);
+  const int32_t n_long = (int32_t)(packed >> 40);
+  int64_t c;
+  const int g = t < R ? split_of(len, plan_args_of(a), total, n_long, &c) : 0;
+  const uint32_t n_multi = g > 1 ? (uint32_t)g : 0u;
+  const uint32_t n_group = g > 1 ? 1u : 0u;
+  const uint32_t n_single = g == 1 ? 1u : 0u;
+  uint32_t tot_m, tot_g, tot_s;
+  const uint32_t off_m = block_exclusive_add(n_multi, sh.scratch, &tot_m);
+  const uint32_t off_g = block_exclusive_add(n_group, sh.scratch, &tot_g);
+  const uint32_t off_s = block_exclusive_add(n_single, sh.scratch, &tot_s);
+  const int G = (int)gridDim.x, B = (int)blockIdx.x;
+  const int num_items = (int)(tot_m + tot_s);
+  if (t < R && g > 1) {
+    // the one split item of this row that falls to this workgroup, if any
+    const int j = B - (int)off_m;
+    if (j >= 0 && j < g) {
+      const int64_t e = (int64_t)(j + 1) * c;
+      WorkItem w;
+      w.row = t;
+      w.begin = (int32_t)(j * c);
+      w.end = (int32_t)(e < len ? e : len);
+      w.group = (int32_t)off_g;
+      w.gsize = g;
+      w.len = len;
+      w.pad[0] = w.pad[1] = 0;
+      sh.pl_items[0] = w;
+    }
+  } else if (t < R) {
+    const int it = (int)tot_m + (int)off_s;
+    const int m = (it - B) / G;
+    if (it % G == B && m < kMaxLocalItems) {
+      WorkItem w;
+      w.row = t;
+      w.begin = 0;
+      w.end = len;
+      w.group = -1;
+      w.gsize = 1;
+      w.len = (len < 0 || (int64_t)len > a.max_len) ? -1 : len;
+      w.pad[0] = w.pad[1] = 0;
+      sh.pl_items[m] = w;
+    }
+  }
+  __syncthreads();
+  // (uniform: workgroup 0 takes the most items)
+  const bool fits = tot_m <= (uint32_t)G && (int)tot_g <= a.max_groups && (num_items - 1) / G < kMaxLocalItems;
+  return fits ? num_items : -1;
+}
+
 template <bool VEC>
 __global__ void __launch_bounds__(kBlock) topk_select_kernel(SelectArgs a) {
   __shared__ Smem sh;
-  // The first item is fetched together with the header (the plan buffer
-  // always holds at least gridDim.x items, so the read stays in bounds; the
-  // item is used only if the header says it exists).
-  const WorkItem first = a.items[blockIdx.x];
-  const PlanHeader h = *a.plan;
-  if (h.magic != kPlanMagic || h.k != a.k || h.grid != (int)gridDim.x || h.num_rows > a.num_rows) {
-    if (threadIdx.x == 0 && blockIdx.x == 0) atomicOr(a.status, TOPK_DEVICE_PLAN_MISMATCH);
-    return;
+  int num_items;
+  WorkItem first{};
+  if (a.plan) {
+    // The first item is fetched together with the header (the plan buffer
+    // always holds at least gridDim.x items, so the read stays in bounds; the
+    // item is used only if the header says it exists).
+    first = a.items[blockIdx.x];
+    const PlanHeader h = *a.plan;
+    if (h.magic != kPlanMagic || h.k != a.k || h.grid != (int)gridDim.x || h.num_rows > a.num_rows) {
+      if (threadIdx.x == 0 && blockIdx.x == 0) atomicOr(a.status, TOPK_DEVICE_PLAN_MISMATCH);
+      return;
+    }
+    num_items = h.num_items;
+  } else {
+    num_items = plan_here(a, sh);
+    if (num_items < 0) {
+      if (threadIdx.x == 0 && blockIdx.x == 0) atomicOr(a.status, TOPK_DEVICE_PLAN_MISMATCH);
+      return;
+    }
   }
-  for (int it = blockIdx.x; it < h.num_items; it += gridDim.x) {
-    const WorkItem w = it == (int)blockIdx.x ? first : a.items[it];
+  for (int it = blockIdx.x; it < num_items; it += gridDim.x) {
+    const WorkItem w = a.plan ? (it == (int)blockIdx.x ? first : a.items[it])
+                              : sh.pl_items[(it - (int)blockIdx.x) / (int)gridDim.x];
     process_item<VEC>(a, w, sh);
     __syncthreads();
   }

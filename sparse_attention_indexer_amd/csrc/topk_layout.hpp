@@ -26,6 +26,10 @@ constexpr int kDefaultMinChunk = 4096;
 constexpr int kDefaultCandCap = kListCap;     // boundary candidates per split row (fits the resolver's LDS)
 
 constexpr uint32_t kPlanMagic = 0x31504B54u;  // "TKP1"
+// Batches of at most this many rows are planned inside the selection kernel
+// (one row per thread; every workgroup derives the same work list), so they
+// need no planning launch and no plan buffer.
+constexpr int kInKernelPlanRows = 512;
 constexpr uint32_t kDefaultSpinLimit = 1u << 21;
 
 // Plan buffer: header, then `capacity` work items.
@@ -112,8 +116,12 @@ struct SelectArgs {
   int32_t* out_slots;
   int32_t* out_idx;       // may be null
   int64_t out_stride;
-  const PlanHeader* plan;
+  const PlanHeader* plan;   // null: plan in the kernel (num_rows <= kInKernelPlanRows)
   const WorkItem* items;
+  int32_t force_path;       // planning inputs, used when plan is null
+  int32_t wg_per_row;
+  int32_t min_chunk;
+  int32_t max_groups;
   GroupState* groups;
   uint64_t* cand;
   int64_t cand_cap;
