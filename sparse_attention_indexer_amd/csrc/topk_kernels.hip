@@ -40,9 +40,10 @@ __device__ __forceinline__ int64_t round_up64(int64_t a, int64_t b) { return cei
 //  - fixed: a fixed group size for every row longer than k;
 //  - force_split: at least 2, the grid's remaining workgroups shared in
 //    proportion to length (at most 2 per row + the rest: fits one round);
-//  - otherwise: the grid shared in proportion to length, floor-rounded so the
-//    split rows' workgroups fit one round of the persistent grid, and no
-//    chunk shorter than min_chunk.
+//  - otherwise: rows that fit one register tile stay whole; longer rows
+//    share the grid in proportion to length, floor-rounded so the split rows'
+//    workgroups fit one round of the persistent grid, and no chunk shorter
+//    than min_chunk.
 // The chunk is then aligned to kChunkAlign, which can only lower the count.
 __device__ __forceinline__ int split_of(int32_t len, const PlanArgs& a, uint64_t total, int32_t n_long,
                                         int64_t* chunk_out) {
@@ -57,6 +58,9 @@ __device__ __forceinline__ int split_of(int32_t len, const PlanArgs& a, uint64_t
   } else if (a.force_path == TOPK_PATH_REGISTER || a.force_path == TOPK_PATH_SINGLE) {
     return 1;
   } else {
+    // A row that fits one workgroup's register tile stays whole: one pass
+    // with no cross-workgroup exchange beats any split of it.
+    if (len <= kTile) return 1;
     g = (int64_t)((uint64_t)a.grid * (uint64_t)len / total);
     const int64_t min_chunk = a.min_chunk > 0 ? a.min_chunk : kDefaultMinChunk;
     const int64_t by_min = len / min_chunk;
@@ -269,6 +273,16 @@ constexpr int kWideWords = kFirstRadixBins + (kFirstRadixBins >> kWidePad);
 constexpr int kWideSlots = kWideWords / 2;          // list entries the padded histogram occupies
 constexpr int kLoadBatch = 24;                      // candidates per lane in flight when the resolver fills LDS
 constexpr int kResolveRegs = 24;                    // candidates per lane of the register-resident first pass
+// While a split row's workgroup waits for the others it re-reads the scores
+// that will probably be needed: those in bins at or above the one holding
+// its own T-th largest score, T = 2 * ceil(k / G) + 64 (twice its share of
+// the row's top k when scores are spread evenly). If the row's threshold bin
+// turns out lower, the workgroup re-reads from the tile instead. Up to
+// kPreRegs per lane; positions are listed in the top of the LDS list, values
+// and block-table entries held in registers.
+constexpr int kPreRegs = 8;
+constexpr int kPreCap = kPreRegs * kBlock;
+constexpr int kStageCap = kListCap - kPreCap / 2;  // staged candidates below the position list
 static_assert(kWideWords * 4 <= kListCap * 8, "first-digit histogram aliases the LDS list");
 static_assert(kMaxK <= kRadixBins, "above-threshold staging aliases rhist");
 
@@ -406,24 +420,53 @@ __device__ __forceinline__ void load_pack(const float* rowp, int32_t base, int32
   }
 }
 
-// Histogram of a packed tile. When one bin takes all 256 scores of a wave's
-// dwordx4 (all-equal or one-bin rows), a single atomic adds 256 instead of
-// 256 conflicting ones. NaN padding lands in an unscanned bin.
-__device__ __forceinline__ void hist_packed(const uint32_t (&hk)[kHk], uint32_t* h) {
+// Histogram of a packed tile into kHistCopies interleaved copies of the
+// 1,024 counters (bin r, copy c at word r * kHistCopies + c; lane l adds to
+// copy l % kHistCopies), so lanes that hit one hot bin in the same
+// instruction mostly land on different words and banks. When one bin takes
+// all 256 scores of a wave's dwordx4 (all-equal or one-bin rows), a single
+// atomic adds 256. NaN padding lands in an unscanned bin; dwordx4 groups
+// wholly past `end` are skipped (the test is uniform across the workgroup).
+constexpr int kHistCopies = 16;
+static_assert(kBins * kHistCopies * 4 <= kListCap * 8, "histogram copies fit in the LDS list region");
+
+__device__ __forceinline__ void hist_packed(const uint32_t (&hk)[kHk], uint32_t* hc, int32_t base, int32_t end) {
+  const uint32_t c = threadIdx.x & (kHistCopies - 1);
 #pragma unroll
   for (int q = 0; q < kEpt / 4; ++q) {
+    if (base + q * kBlock * 4 >= end) break;
     const uint32_t p0 = hk[2 * q], p1 = hk[2 * q + 1];
     const uint32_t r0 = (p0 >> 6) & 0x3FFu, r1 = p0 >> 22, r2 = (p1 >> 6) & 0x3FFu, r3 = p1 >> 22;
     const uint32_t f = (uint32_t)__builtin_amdgcn_readfirstlane((int)r0);
     const bool same = r0 == f && r1 == f && r2 == f && r3 == f;
     if (__ballot(same) == ~0ull) {
-      if (lane() == 0) atomicAdd(&h[f], 256u);
+      if (lane() == 0) atomicAdd(&hc[f * kHistCopies + c], 256u);
     } else {
-      atomicAdd(&h[r0], 1u);
-      atomicAdd(&h[r1], 1u);
-      atomicAdd(&h[r2], 1u);
-      atomicAdd(&h[r3], 1u);
+      atomicAdd(&hc[r0 * kHistCopies + c], 1u);
+      atomicAdd(&hc[r1 * kHistCopies + c], 1u);
+      atomicAdd(&hc[r2 * kHistCopies + c], 1u);
+      atomicAdd(&hc[r3 * kHistCopies + c], 1u);
     }
+  }
+}
+
+// Zero the histogram copies (whole workgroup; a barrier must follow).
+__device__ __forceinline__ void hist_copies_clear(uint32_t* hc) {
+  uint4* p = reinterpret_cast<uint4*>(hc);
+  for (int i = threadIdx.x; i < kBins * kHistCopies / 4; i += kBlock) p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Sum the copies into h[0, kBins) (whole workgroup; a barrier must follow).
+__device__ __forceinline__ void hist_copies_sum(const uint32_t* hc, uint32_t* h) {
+  for (int r = threadIdx.x; r < kBins; r += kBlock) {
+    const uint4* p = reinterpret_cast<const uint4*>(hc + r * kHistCopies);
+    uint32_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < kHistCopies / 4; ++i) {
+      const uint4 v = p[i];
+      sum += v.x + v.y + v.z + v.w;
+    }
+    h[r] = sum;
   }
 }
 
@@ -488,6 +531,24 @@ __device__ __forceinline__ void extract(uint64_t mask, int32_t base, const float
         on_cand(kk, e[u]);
       }
     }
+  }
+}
+
+// One position whose FP32 score x may lie at or above the threshold bin:
+// above it -> on_above(position, page); in it -> range and on_cand.
+template <class A, class C>
+__device__ __forceinline__ void classify(float x, int32_t e, int32_t pg, Cut cut, Range& rg, A&& on_above,
+                                         C&& on_cand) {
+  const _Float16 h = half_lo(to_half2(x, x));
+  if (h >= cut.vhi) {
+    on_above(e, pg);
+  } else if (h >= cut.vlo) {
+    const uint32_t kk = key32_of(x);
+    rg.kmax = max(rg.kmax, kk);
+    rg.kmin_inv = max(rg.kmin_inv, ~kk);
+    rg.imax = max(rg.imax, (uint32_t)e);
+    rg.imin_inv = max(rg.imin_inv, ~(uint32_t)e);
+    on_cand(kk, e);
   }
 }
 
@@ -603,7 +664,12 @@ struct PairListSrc {
   }
 };
 
-// Threshold-bin scores of [begin, end), re-read from the row.
+// Threshold-bin scores of [begin, end), re-read from the row. Each step
+// loads kStreamVec dwordx4 per lane (all in flight together) before using
+// any of them, so a pass over the row is a few long bursts rather than many
+// short round trips.
+constexpr int kStreamVec = 8;
+
 template <bool VEC>
 struct StreamSrc {
   const float* rowp;
@@ -612,10 +678,10 @@ struct StreamSrc {
   Refine r;
   template <class F>
   __device__ __forceinline__ void each(F&& f) const {
-    for (int32_t base = begin; base < end; base += 2 * kBlock * 4) {
-      float x[8];
+    for (int32_t base = begin; base < end; base += kStreamVec * kBlock * 4) {
+      float x[kStreamVec * 4];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < kStreamVec; ++u) {
         const int32_t e = base + (u * kBlock + (int)threadIdx.x) * 4;
 #pragma unroll
         for (int c = 0; c < 4; ++c) x[u * 4 + c] = 0.f;
@@ -634,7 +700,7 @@ struct StreamSrc {
         }
       }
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < kStreamVec; ++u)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int32_t e = base + (u * kBlock + (int)threadIdx.x) * 4 + c;
@@ -1042,8 +1108,43 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
   }
   drain_memory();
   __syncthreads();
+  if (t == 0) __hip_atomic_fetch_add(&g->arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // While the other workgroups arrive: list the positions at or above the
+  // local k-th bin and start reading their scores and block-table entries.
+  uint32_t* pre = reinterpret_cast<uint32_t*>(sh.list + kStageCap);
+  float pv[kPreRegs];
+  int32_t ppg[kPreRegs];
+  uint32_t n_pre = 0xFFFFFFFFu, bpre = kNotFound;
+  if (resident) {
+    const uint32_t T = min(k, 2u * ((k + G - 1u) / G) + 64u);
+    if (t == 0) sh.res[0] = 0;
+    if ((uint32_t)(end - begin) >= T) find_threshold_raw(sh.lhist, T, sh.scratch, sh.res);
+    else __syncthreads();
+    bpre = uni(sh.res[0]);
+    const uint64_t pm = interest_mask(hk, cut_of_bin(bpre).vlo);
+    uint32_t tot;
+    uint32_t off = block_exclusive_add((uint32_t)__popcll(pm), sh.scratch, &tot);
+    n_pre = uni(tot);
+    if (n_pre <= (uint32_t)kPreCap) {
+      uint64_t m = pm;
+      while (m) {
+        const int j = __builtin_ctzll(m);
+        m &= m - 1ull;
+        pre[off++] = (uint32_t)tile_pos(begin, j >> 2, j & 3);
+      }
+    }
+    __syncthreads();
+    if (n_pre <= (uint32_t)kPreCap) {
+#pragma unroll
+      for (int i = 0; i < kPreRegs; ++i) {
+        const uint32_t idx = (uint32_t)(t + i * kBlock);
+        const int32_t e = idx < n_pre ? (int32_t)pre[idx] : begin;
+        pv[i] = idx < n_pre ? rowp[e] : 0.f;
+        ppg[i] = idx < n_pre ? o.page(e) : 0;
+      }
+    }
+  }
   if (t == 0) {
-    __hip_atomic_fetch_add(&g->arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t spins = 0, ok = 1;
     while (ld_agent(&g->arrive) < G) {
       __builtin_amdgcn_s_sleep(1);
@@ -1081,7 +1182,7 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
   local_above = uni(local_above);
   const uint32_t local_cnt = found ? uni(sh.lhist[raw_of_bin(bstar)]) : 0u;
   const bool keep = found && (int64_t)cnt <= a.cand_cap;
-  const bool stage = keep && local_cnt <= (uint32_t)kListCap;   // candidates staged in LDS
+  const bool stage = keep && local_cnt <= (uint32_t)kStageCap;   // candidates staged in LDS
   // This workgroup's output and candidate offsets in the row; their round
   // trips overlap the re-reads of the extraction below.
   // (Only the rare unstaged case, candidates written straight to global
@@ -1115,13 +1216,21 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
     if (!keep) return;
     const uint32_t c = atomicAdd(&sh.cur_list, 1u);
     const uint64_t v = ((uint64_t)kk << 32) | (uint32_t)e;
-    const bool ok = stage ? c < (uint32_t)kListCap : (int64_t)c < a.cand_cap;
+    const bool ok = stage ? c < (uint32_t)kStageCap : (int64_t)c < a.cand_cap;
     if (ok && stage) sh.list[c] = v;
     if (ok && !stage) st_agent(slab + c, v);
     bad |= !ok;
   };
   if (found) {
-    if (resident) {
+    if (resident && n_pre <= (uint32_t)kPreCap && bstar >= bpre) {
+      // Every position at or above the row's threshold bin was pre-read.
+#pragma unroll
+      for (int i = 0; i < kPreRegs; ++i) {
+        const uint32_t idx = (uint32_t)(t + i * kBlock);
+        if (idx < n_pre) classify(pv[i], (int32_t)pre[idx], ppg[i], cut, rg, on_above, on_cand);
+      }
+    } else if (resident) {
+      load_pack<VEC>(rowp, begin, end, hk);   // (the tile is not held across the wait)
       extract(interest_mask(hk, cut.vlo), begin, rowp, cut.vhi, rg, on_above, on_cand, &o);
     } else {
       for (int32_t base = begin; base < end; base += kTile) {
@@ -1148,7 +1257,7 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
   const uint32_t n_out = min(uni(sh.cur_out), (uint32_t)kMaxK);
   for (uint32_t i = t; i < n_out; i += kBlock) bad |= !o.store_page(bo + i, (int32_t)staged[i], (int32_t)staged_pg[i]);
   if (stage) {
-    const uint32_t n_c = min(uni(sh.cur_list), (uint32_t)kListCap);
+    const uint32_t n_c = min(uni(sh.cur_list), (uint32_t)kStageCap);
     for (uint32_t i = t; i < n_c; i += kBlock) {
       const bool ok = (int64_t)(bc + i) < a.cand_cap;
       if (ok) st_agent(slab + bc + i, sh.list[i]);
@@ -1213,17 +1322,20 @@ __device__ __forceinline__ void process_item(const SelectArgs& a, const WorkItem
   const int32_t begin = w.begin, end = min(w.end, len);
   const bool resident = end - begin <= kTile;
   uint32_t hk[kHk];
-  for (int i = t; i < kBins; i += kBlock) sh.lhist[i] = 0;
+  uint32_t* hc = reinterpret_cast<uint32_t*>(sh.list);   // free until the extraction
+  hist_copies_clear(hc);
   __syncthreads();
   if (resident) {
     load_pack<VEC>(rowp, begin, end, hk);
-    hist_packed(hk, sh.lhist);
+    hist_packed(hk, hc, begin, end);
   } else {
     for (int32_t base = begin; base < end; base += kTile) {
       load_pack<VEC>(rowp, base, end, hk);
-      hist_packed(hk, sh.lhist);
+      hist_packed(hk, hc, base, end);
     }
   }
+  __syncthreads();
+  hist_copies_sum(hc, sh.lhist);
   __syncthreads();
   if (w.group < 0) owned_row<VEC>(a, len, rowp, o, resident, hk, sh);
   else split_row<VEC>(a, w, len, rowp, o, resident, hk, sh);
