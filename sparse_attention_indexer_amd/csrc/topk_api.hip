@@ -132,7 +132,7 @@ topk_status topk_plan(const topk_config* cfg, const int32_t* lengths, int32_t nu
   if (num_rows < 0 || num_rows > cfg->max_rows || !plan) return TOPK_ERR_INVALID_ARG;
   if (num_rows > 0 && !lengths) return TOPK_ERR_INVALID_ARG;
   if (plan_bytes < s.plan_bytes) return TOPK_ERR_BUFFER_TOO_SMALL;
-  if (num_rows <= kInKernelPlanRows) return TOPK_OK;   // the selection kernel plans these itself
+  if (num_rows <= kInKernelPlanRows && s.grid < 4096) return TOPK_OK;   // the selection kernel plans these itself
   const bool no_split = cfg->force_path == TOPK_PATH_REGISTER || cfg->force_path == TOPK_PATH_SINGLE;
   PlanArgs a;
   a.lengths = lengths;
@@ -165,7 +165,7 @@ topk_status select_impl(const topk_config* cfg, const void* plan, const float* s
   if (num_rows < 0 || num_rows > cfg->max_rows) return TOPK_ERR_INVALID_ARG;
   if (page_size < 1 || bt_row_stride < 0 || out_row_stride < cfg->k) return TOPK_ERR_INVALID_ARG;
   if (score_row_stride < cfg->max_len || score_row_stride < 0) return TOPK_ERR_INVALID_ARG;
-  if ((!plan && num_rows > kInKernelPlanRows) || !workspace) return TOPK_ERR_INVALID_ARG;
+  if ((!plan && (num_rows > kInKernelPlanRows || s.grid >= 4096)) || !workspace) return TOPK_ERR_INVALID_ARG;
   if (num_rows > 0 && (!scores || !lengths || !block_table || !out_slots)) return TOPK_ERR_INVALID_ARG;
   if (workspace_bytes < s.workspace_bytes) return TOPK_ERR_BUFFER_TOO_SMALL;
   if (num_rows == 0) return TOPK_OK;
@@ -187,7 +187,7 @@ topk_status select_impl(const topk_config* cfg, const void* plan, const float* s
   a.out_slots = out_slots;
   a.out_idx = out_indices;
   a.out_stride = out_row_stride;
-  const bool here = num_rows <= kInKernelPlanRows;
+  const bool here = num_rows <= kInKernelPlanRows && s.grid < 4096;   // the in-kernel scan packs 12-bit item counts
   a.plan = here ? nullptr : (const PlanHeader*)plan;
   a.items = here ? nullptr : (const WorkItem*)((const char*)plan + sizeof(PlanHeader));
   a.force_path = cfg->force_path;

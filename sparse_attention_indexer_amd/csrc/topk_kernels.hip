@@ -393,23 +393,34 @@ __device__ __forceinline__ int32_t tile_pos(int32_t base, int q, int c) {
 
 constexpr int kHk = kEpt / 2;   // packed registers per lane
 
+// A tile's raw dwordx4 loads: lane t's vector q holds positions
+// tile_pos(base, q, 0..3); vectors that start at or past `end` are not read.
 template <bool VEC>
-__device__ __forceinline__ void load_pack(const float* rowp, int32_t base, int32_t end, uint32_t (&hk)[kHk]) {
+__device__ __forceinline__ void load_raw(const float* rowp, int32_t base, int32_t end, float4 (&x)[kEpt / 4]) {
 #pragma unroll
   for (int q = 0; q < kEpt / 4; ++q) {
     const int32_t e = tile_pos(base, q, 0);
-    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    x[q] = make_float4(0.f, 0.f, 0.f, 0.f);
     if constexpr (VEC) {
       // Rows are 16-byte aligned and their stride is a multiple of 4, so a
       // vector that starts before `end` lies inside the row.
-      if (e < end) x = *reinterpret_cast<const float4*>(rowp + e);
+      if (e < end) x[q] = *reinterpret_cast<const float4*>(rowp + e);
     } else {
-      if (e < end) x.x = rowp[e];
-      if (e + 1 < end) x.y = rowp[e + 1];
-      if (e + 2 < end) x.z = rowp[e + 2];
-      if (e + 3 < end) x.w = rowp[e + 3];
+      if (e < end) x[q].x = rowp[e];
+      if (e + 1 < end) x[q].y = rowp[e + 1];
+      if (e + 2 < end) x[q].z = rowp[e + 2];
+      if (e + 3 < end) x[q].w = rowp[e + 3];
     }
-    uint32_t p0 = to_half2(x.x, x.y), p1 = to_half2(x.z, x.w);
+  }
+}
+
+// Raw loads -> packed FP16 tile; positions at or past `end` become NaN.
+__device__ __forceinline__ void pack_tile(const float4 (&x)[kEpt / 4], int32_t base, int32_t end,
+                                          uint32_t (&hk)[kHk]) {
+#pragma unroll
+  for (int q = 0; q < kEpt / 4; ++q) {
+    const int32_t e = tile_pos(base, q, 0);
+    uint32_t p0 = to_half2(x[q].x, x[q].y), p1 = to_half2(x[q].z, x[q].w);
     if (e + 4 > end) {  // tail vector: positions >= end become NaN
       const int n = end - e;
       p0 = n <= 0 ? kHalfNaN2 : (n == 1 ? (p0 & 0xFFFFu) | (kHalfNaN << 16) : p0);
@@ -418,6 +429,13 @@ __device__ __forceinline__ void load_pack(const float* rowp, int32_t base, int32
     hk[2 * q] = p0;
     hk[2 * q + 1] = p1;
   }
+}
+
+template <bool VEC>
+__device__ __forceinline__ void load_pack(const float* rowp, int32_t base, int32_t end, uint32_t (&hk)[kHk]) {
+  float4 x[kEpt / 4];
+  load_raw<VEC>(rowp, base, end, x);
+  pack_tile(x, base, end, hk);
 }
 
 // Histogram of a packed tile into kHistCopies interleaved copies of the
@@ -1185,19 +1203,23 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
   const bool stage = keep && local_cnt <= (uint32_t)kStageCap;   // candidates staged in LDS
   // This workgroup's output and candidate offsets in the row; their round
   // trips overlap the re-reads of the extraction below.
-  // (Only the rare unstaged case, candidates written straight to global
-  // memory, needs its base before the extraction; otherwise thread 0 reads
-  // the atomics' results after it.)
+  // Thread 0 uses the atomics' results only after the extraction (nothing
+  // before that barrier may depend on them, or the whole workgroup would wait
+  // for the round trip); only the rare unstaged case, candidates written
+  // straight to global memory, needs its base first.
   uint32_t base_out = 0, base_cand = 0;
   if (t == 0) {
+    sh.cur_out = 0;
+    sh.cur_list = 0;
+    sh.range[0] = sh.range[1] = sh.range[2] = sh.range[3] = 0;
     if (local_above) base_out = __hip_atomic_fetch_add(&g->emit, local_above, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (keep && local_cnt) base_cand = __hip_atomic_fetch_add(&g->cand, local_cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sh.cur_out = 0;
-    sh.range[0] = sh.range[1] = sh.range[2] = sh.range[3] = 0;
-    if (keep && !stage) sh.cur_list = base_cand;
-    else sh.cur_list = 0u;
   }
   __syncthreads();
+  if (keep && !stage) {
+    if (t == 0) sh.cur_list = base_cand;
+    __syncthreads();
+  }
   uint64_t* slab = a.cand + (int64_t)w.group * a.cand_cap;
   uint32_t* staged = sh.rhist;     // positions above the threshold bin (< k of them)
   uint32_t* staged_pg = sh.outpos; // and their block-table entries
@@ -1286,8 +1308,17 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
   }
 }
 
+// The packed register tile parked in the upper half of the LDS list (lane
+// t's register i at word i * kBlock + t), clear of the histogram copies.
+__device__ __forceinline__ uint32_t* parked_tile(Smem& sh) {
+  return reinterpret_cast<uint32_t*>(sh.list + kListCap / 2);
+}
+static_assert(kHk * kBlock * 4 <= kListCap / 2 * 8, "a parked tile fits in half the LDS list");
+static_assert(kBins * kHistCopies * 4 <= kListCap / 2 * 8, "histogram copies fit below a parked tile");
+
+// parked: this item's register tile is already in LDS (parked_tile).
 template <bool VEC>
-__device__ __forceinline__ void process_item(const SelectArgs& a, const WorkItem& w, Smem& sh) {
+__device__ __forceinline__ void process_item(const SelectArgs& a, const WorkItem& w, Smem& sh, bool parked = false) {
   const int t = threadIdx.x;
   const int row = w.row;
   const int32_t len = w.len;   // planned from the same lengths (one dependent load fewer)
@@ -1326,7 +1357,13 @@ __device__ __forceinline__ void process_item(const SelectArgs& a, const WorkItem
   hist_copies_clear(hc);
   __syncthreads();
   if (resident) {
-    load_pack<VEC>(rowp, begin, end, hk);
+    if (parked) {
+      const uint32_t* pt = parked_tile(sh);
+#pragma unroll
+      for (int i = 0; i < kHk; ++i) hk[i] = pt[i * kBlock + t];
+    } else {
+      load_pack<VEC>(rowp, begin, end, hk);
+    }
     hist_packed(hk, hc, begin, end);
   } else {
     for (int32_t base = begin; base < end; base += kTile) {
@@ -1380,13 +1417,14 @@ __device__ __forceinline__ int plan_here(const SelectArgs& a, Smem& sh) {
   const int32_t n_long = (int32_t)(packed >> 40);
   int64_t c;
   const int g = t < R ? split_of(len, plan_args_of(a), total, n_long, &c) : 0;
-  const uint32_t n_multi = g > 1 ? (uint32_t)g : 0u;
-  const uint32_t n_group = g > 1 ? 1u : 0u;
-  const uint32_t n_single = g == 1 ? 1u : 0u;
-  uint32_t tot_m, tot_g, tot_s;
-  const uint32_t off_m = block_exclusive_add(n_multi, sh.scratch, &tot_m);
-  const uint32_t off_g = block_exclusive_add(n_group, sh.scratch, &tot_g);
-  const uint32_t off_s = block_exclusive_add(n_single, sh.scratch, &tot_s);
+  // One scan of three packed counts: split items (12 bits: at most the
+  // grid, which the host keeps below 4096 for this path), split rows and
+  // whole rows (10 bits each: at most kInKernelPlanRows).
+  const uint32_t packed_n = (g > 1 ? (uint32_t)g | (1u << 12) : 0u) | (g == 1 ? 1u << 22 : 0u);
+  uint32_t packed_tot;
+  const uint32_t packed_off = block_exclusive_add(packed_n, sh.scratch, &packed_tot);
+  const uint32_t off_m = packed_off & 0xFFFu, off_g = (packed_off >> 12) & 0x3FFu, off_s = packed_off >> 22;
+  const uint32_t tot_m = packed_tot & 0xFFFu, tot_g = (packed_tot >> 12) & 0x3FFu, tot_s = packed_tot >> 22;
   const int G = (int)gridDim.x, B = (int)blockIdx.x;
   const int num_items = (int)(tot_m + tot_s);
   if (t < R && g > 1) {
@@ -1430,6 +1468,7 @@ __global__ void __launch_bounds__(kBlock) topk_select_kernel(SelectArgs a) {
   __shared__ Smem sh;
   int num_items;
   WorkItem first{};
+  bool parked = false;
   if (a.plan) {
     // The first item is fetched together with the header (the plan buffer
     // always holds at least gridDim.x items, so the read stays in bounds; the
@@ -1442,16 +1481,54 @@ __global__ void __launch_bounds__(kBlock) topk_select_kernel(SelectArgs a) {
     }
     num_items = h.num_items;
   } else {
+    // Start loading this workgroup's tile as planned for a batch whose rows
+    // all have max_len scores, before the lengths arrive; the loads are used
+    // when the real plan gives the same chunk (every batch of equal lengths).
+    float4 x[kEpt / 4];
+    int32_t srow = -1, sbeg = 0, send = 0;
+    // (uniform across the workgroup: every value below derives from kernel
+    // arguments and blockIdx)
+    {
+      const int32_t L = (int32_t)a.max_len;
+      const uint64_t total = L > a.k ? (uint64_t)L * (uint64_t)a.num_rows : 0ull;
+      int64_t c;
+      const int g = split_of(L, plan_args_of(a), total, L > a.k ? a.num_rows : 0, &c);
+      const int B = (int)blockIdx.x;
+      if (g > 1 && B < a.num_rows * g) {
+        srow = B / g;
+        sbeg = (int32_t)((B % g) * c);
+        send = (int32_t)min((int64_t)sbeg + c, (int64_t)L);
+      } else if (g <= 1 && L > a.k && B < a.num_rows) {
+        srow = B;
+        send = L;
+      }
+      if (srow >= 0 && send - sbeg <= kTile) load_raw<VEC>(a.scores + (int64_t)srow * a.stride, sbeg, send, x);
+      else srow = -1;
+    }
     num_items = plan_here(a, sh);
     if (num_items < 0) {
       if (threadIdx.x == 0 && blockIdx.x == 0) atomicOr(a.status, TOPK_DEVICE_PLAN_MISMATCH);
       return;
     }
+    // Park the tile if the real plan gave the guessed chunk (the same row and
+    // start, ending no later; positions past the real end become NaN).
+    if ((int)blockIdx.x < num_items && srow >= 0) {
+      const WorkItem w0 = sh.pl_items[0];
+      const int32_t end0 = min(w0.end, w0.len);
+      parked = w0.row == srow && w0.begin == sbeg && end0 <= send && w0.len > a.k && (int64_t)w0.len <= a.max_len;
+      if (parked) {
+        uint32_t hk[kHk];
+        pack_tile(x, sbeg, end0, hk);
+        uint32_t* pt = parked_tile(sh);
+#pragma unroll
+        for (int i = 0; i < kHk; ++i) pt[i * kBlock + threadIdx.x] = hk[i];
+      }
+    }
   }
   for (int it = blockIdx.x; it < num_items; it += gridDim.x) {
     const WorkItem w = a.plan ? (it == (int)blockIdx.x ? first : a.items[it])
                               : sh.pl_items[(it - (int)blockIdx.x) / (int)gridDim.x];
-    process_item<VEC>(a, w, sh);
+    process_item<VEC>(a, w, sh, parked && it == (int)blockIdx.x);
     __syncthreads();
   }
 }
