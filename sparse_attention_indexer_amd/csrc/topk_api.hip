@@ -13,7 +13,8 @@ static_assert(satopk::kInKernelPlanRows <= satopk::kBlock, "one row per thread")
 
 namespace satopk {
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
-hipError_t launch_select(const SelectArgs& a, int grid, bool vec, hipStream_t s, hipEvent_t start, hipEvent_t stop);
+hipError_t launch_select(const SelectArgs& a, int grid, bool vec, bool stream_items, hipStream_t s, hipEvent_t start,
+                         hipEvent_t stop);
 hipError_t launch_fill(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_debug_keys(const float* x, int64_t n, uint32_t* bin, uint32_t* k32, hipStream_t s);
 hipError_t select_occupancy(int* per_cu);
@@ -103,6 +104,19 @@ topk_status sizing(const topk_config* cfg, Sizing* s) {
   s->plan_bytes = sizeof(PlanHeader) + sizeof(WorkItem) * (size_t)s->max_items;
   s->workspace_bytes = ws_total_bytes(*s);
   return TOPK_OK;
+}
+
+// Whether some work item can exceed one register tile. With the planner's
+// defaults every row longer than a tile gets at least one workgroup per tile
+// when the rows' tile counts fit the grid, which max_rows * ceil(max_len /
+// tile) bounds; forced paths, fixed group sizes and large minimum chunks can
+// still produce longer items.
+bool items_may_stream(const topk_config* cfg, const Sizing& s) {
+  if (cfg->max_len <= kTile) return false;
+  if (cfg->force_path == TOPK_PATH_REGISTER) return false;   // max_len <= kTile is enforced
+  if (cfg->force_path != TOPK_PATH_AUTO || cfg->wg_per_row > 0 || cfg->min_chunk > kTile) return true;
+  const int64_t tiles = (cfg->max_len + kTile - 1) / kTile;
+  return (int64_t)cfg->max_rows * tiles > s.grid;
 }
 
 }  // namespace
@@ -201,7 +215,8 @@ topk_status select_impl(const topk_config* cfg, const void* plan, const float* s
   a.max_len = cfg->max_len;
   a.spin_limit = kDefaultSpinLimit;
   const bool vec = ((uintptr_t)scores % 16 == 0) && (score_row_stride % 4 == 0);
-  return launch_select(a, s.grid, vec, (hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event) ==
+  return launch_select(a, s.grid, vec, items_may_stream(cfg, s), (hipStream_t)stream, (hipEvent_t)start_event,
+                       (hipEvent_t)stop_event) ==
                  hipSuccess
              ? TOPK_OK
              : TOPK_ERR_HIP;

@@ -72,6 +72,11 @@ __device__ __forceinline__ uint32_t wave_inclusive_add(uint32_t x) {
   return x;
 }
 
+// Sum over the wave (every lane receives it).
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_add(x), 63);
+}
+
 // Maximum over the wave (every lane receives it).
 __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
   x = max(x, SATOPK_DPP(x, 0x111, 0xf));

@@ -40,13 +40,23 @@ __device__ __forceinline__ int64_t round_up64(int64_t a, int64_t b) { return cei
 //  - fixed: a fixed group size for every row longer than k;
 //  - force_split: at least 2, the grid's remaining workgroups shared in
 //    proportion to length (at most 2 per row + the rest: fits one round);
-//  - otherwise: rows that fit one register tile stay whole; longer rows
-//    share the grid in proportion to length, floor-rounded so the split rows'
-//    workgroups fit one round of the persistent grid, and no chunk shorter
-//    than min_chunk.
+//  - otherwise: rows that fit one register tile stay whole; each takes one
+//    item, and the rest of the grid (the budget) goes to the longer rows.
+//    A longer row first gets one workgroup per register tile it spans (so
+//    every chunk stays register-resident), when those add up to no more than
+//    the budget (`tiles` is their sum over the batch); the rest of the budget
+//    is shared in proportion to length, floor-rounded, so all items fit one
+//    round of the persistent grid, with no chunk shorter than min_chunk.
+// `total` and `n_long` sum over the rows this mode splits: longer than one
+// tile by default, longer than k under a forced split or fixed group size.
 // The chunk is then aligned to kChunkAlign, which can only lower the count.
+__device__ __forceinline__ int64_t tiles_of(int32_t len) { return len > kTile ? ceil_div64(len, kTile) : 0; }
+__device__ __forceinline__ int32_t split_floor(const PlanArgs& a) {
+  return (a.force_path == TOPK_PATH_AUTO && a.wg_per_row <= 0) ? max(kTile, a.k) : a.k;
+}
+
 __device__ __forceinline__ int split_of(int32_t len, const PlanArgs& a, uint64_t total, int32_t n_long,
-                                        int64_t* chunk_out) {
+                                        uint32_t tiles, int64_t* chunk_out) {
   *chunk_out = len;
   if (len <= a.k || total == 0) return 1;
   int64_t g;
@@ -61,7 +71,11 @@ __device__ __forceinline__ int split_of(int32_t len, const PlanArgs& a, uint64_t
     // A row that fits one workgroup's register tile stays whole: one pass
     // with no cross-workgroup exchange beats any split of it.
     if (len <= kTile) return 1;
-    g = (int64_t)((uint64_t)a.grid * (uint64_t)len / total);
+    const int64_t budget = (int64_t)a.grid - ((int64_t)a.num_rows - n_long);
+    if (budget >= (int64_t)tiles)
+      g = tiles_of(len) + (int64_t)((uint64_t)(budget - (int64_t)tiles) * (uint64_t)len / total);
+    else
+      g = (int64_t)((uint64_t)a.grid * (uint64_t)len / total);
     const int64_t min_chunk = a.min_chunk > 0 ? a.min_chunk : kDefaultMinChunk;
     const int64_t by_min = len / min_chunk;
     if (g > by_min) g = by_min;
@@ -78,6 +92,7 @@ constexpr int kPlanWaves = kPlanBlock / 64;
 
 __global__ void __launch_bounds__(kPlanBlock) topk_plan_kernel(PlanArgs a) {
   __shared__ uint64_t s_red[kPlanWaves];
+  __shared__ uint64_t s_red2[kPlanWaves];
   __shared__ uint32_t s_scan[kPlanWaves];
   __shared__ int s_carry_multi, s_carry_groups, s_carry_single;
   const int t = threadIdx.x;
@@ -86,19 +101,30 @@ __global__ void __launch_bounds__(kPlanBlock) topk_plan_kernel(PlanArgs a) {
   // LDS word per wave: no same-address atomics).
   uint64_t mine = 0;
   uint32_t longs = 0;
+  uint64_t tl = 0;
+  const int32_t floor_len = split_floor(a);
   for (int r = t; r < a.num_rows; r += kPlanBlock) {
     const int32_t len = a.lengths[r];
-    if (len > a.k) {
+    if (len > floor_len) {
       mine += (uint64_t)len;
       ++longs;
+      tl += (uint64_t)tiles_of(len);
     }
   }
   mine = wave_sum_u64(mine + ((uint64_t)longs << 40));   // lengths < 2^31, rows < 2^23
-  if (lane() == 0) s_red[t >> 6] = mine;
+  tl = wave_sum_u64(tl);
+  if (lane() == 0) {
+    s_red[t >> 6] = mine;
+    s_red2[t >> 6] = tl;
+  }
   __syncthreads();
-  uint64_t packed = 0;
+  uint64_t packed = 0, tiles64 = 0;
 #pragma unroll
-  for (int i = 0; i < kPlanWaves; ++i) packed += s_red[i];
+  for (int i = 0; i < kPlanWaves; ++i) {
+    packed += s_red[i];
+    tiles64 += s_red2[i];
+  }
+  const uint32_t tiles = (uint32_t)min(tiles64, (uint64_t)0xFFFFFFFFu);   // saturated: > grid either way
   const uint64_t total = packed & ((1ull << 40) - 1);
   const int32_t n_long = (int32_t)(packed >> 40);
   if (t == 0) {
@@ -114,7 +140,7 @@ __global__ void __launch_bounds__(kPlanBlock) topk_plan_kernel(PlanArgs a) {
   uint32_t my_multi = 0, my_groups = 0;
   for (int r = t; r < a.num_rows; r += kPlanBlock) {
     int64_t c;
-    const int g = split_of(a.lengths[r], a, total, n_long, &c);
+    const int g = split_of(a.lengths[r], a, total, n_long, tiles, &c);
     if (g > 1) {
       my_multi += (uint32_t)g;
       my_groups += 1;
@@ -140,7 +166,7 @@ __global__ void __launch_bounds__(kPlanBlock) topk_plan_kernel(PlanArgs a) {
     int32_t len = 0;
     if (r < a.num_rows) {
       len = a.lengths[r];
-      g = split_of(len, a, total, n_long, &c);
+      g = split_of(len, a, total, n_long, tiles, &c);
     }
     const uint32_t n_multi = (r < a.num_rows && g > 1) ? (uint32_t)g : 0u;
     const uint32_t n_group = n_multi ? 1u : 0u;
@@ -303,6 +329,7 @@ struct __align__(16) Smem {
   uint32_t range[4];            // candidate key/position range: kmax, ~kmin, imax, ~imin
   uint32_t bcast[4];
   uint64_t pl_red[kWaves];
+  uint32_t pl_red2[kWaves];
   WorkItem pl_items[kMaxLocalItems];   // in-kernel plan: this workgroup's items, in loop order
 };
 
@@ -454,6 +481,53 @@ __device__ __forceinline__ void hist_packed(const uint32_t (&hk)[kHk], uint32_t*
   for (int q = 0; q < kEpt / 4; ++q) {
     if (base + q * kBlock * 4 >= end) break;
     const uint32_t p0 = hk[2 * q], p1 = hk[2 * q + 1];
+    const uint32_t r0 = (p0 >> 6) & 0x3FFu, r1 = p0 >> 22, r2 = (p1 >> 6) & 0x3FFu, r3 = p1 >> 22;
+    const uint32_t f = (uint32_t)__builtin_amdgcn_readfirstlane((int)r0);
+    const bool same = r0 == f && r1 == f && r2 == f && r3 == f;
+    if (__ballot(same) == ~0ull) {
+      if (lane() == 0) atomicAdd(&hc[f * kHistCopies + c], 256u);
+    } else {
+      atomicAdd(&hc[r0 * kHistCopies + c], 1u);
+      atomicAdd(&hc[r1 * kHistCopies + c], 1u);
+      atomicAdd(&hc[r2 * kHistCopies + c], 1u);
+      atomicAdd(&hc[r3 * kHistCopies + c], 1u);
+    }
+  }
+}
+
+// N dwordx4 per lane at positions base + (u * kBlock + t) * 4 (vectors that
+// start at or past `end` are not read), and their histogram (same layout and
+// fast path as hist_packed; positions past `end` are NaN).
+template <bool VEC, int N>
+__device__ __forceinline__ void load_vecs(const float* rowp, int32_t base, int32_t end, float4 (&x)[N]) {
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    const int32_t e = base + (u * kBlock + (int)threadIdx.x) * 4;
+    x[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if constexpr (VEC) {
+      if (e < end) x[u] = *reinterpret_cast<const float4*>(rowp + e);
+    } else {
+      if (e < end) x[u].x = rowp[e];
+      if (e + 1 < end) x[u].y = rowp[e + 1];
+      if (e + 2 < end) x[u].z = rowp[e + 2];
+      if (e + 3 < end) x[u].w = rowp[e + 3];
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void hist_vecs(const float4 (&x)[N], uint32_t* hc, int32_t base, int32_t end) {
+  const uint32_t c = threadIdx.x & (kHistCopies - 1);
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    if (base + u * kBlock * 4 >= end) break;
+    const int32_t e = base + (u * kBlock + (int)threadIdx.x) * 4;
+    uint32_t p0 = to_half2(x[u].x, x[u].y), p1 = to_half2(x[u].z, x[u].w);
+    if (e + 4 > end) {
+      const int n = end - e;
+      p0 = n <= 0 ? kHalfNaN2 : (n == 1 ? (p0 & 0xFFFFu) | (kHalfNaN << 16) : p0);
+      p1 = n <= 2 ? kHalfNaN2 : (n == 3 ? (p1 & 0xFFFFu) | (kHalfNaN << 16) : p1);
+    }
     const uint32_t r0 = (p0 >> 6) & 0x3FFu, r1 = p0 >> 22, r2 = (p1 >> 6) & 0x3FFu, r3 = p1 >> 22;
     const uint32_t f = (uint32_t)__builtin_amdgcn_readfirstlane((int)r0);
     const bool same = r0 == f && r1 == f && r2 == f && r3 == f;
@@ -1003,9 +1077,27 @@ __device__ __forceinline__ void owned_row(const SelectArgs& a, int32_t len, cons
   if (resident) {
     extract(interest_mask(hk, cut.vlo), 0, rowp, cut.vhi, rg, on_above, on_cand);
   } else {
+    // Streamed row. When many of its scores lie at or above the threshold
+    // bin (dense boundary bins), each tile is read again whole and
+    // classified from the FP32 registers; otherwise the tile is binned again
+    // and only its few such positions are re-read.
+    const bool dense = (uint64_t)(n_above + cnt) * 8u > (uint64_t)len;
     for (int32_t base = 0; base < len; base += kTile) {
-      load_pack<VEC>(rowp, base, len, hk);
-      extract(interest_mask(hk, cut.vlo), base, rowp, cut.vhi, rg, on_above, on_cand);
+      if (dense) {
+        float4 x[kEpt / 4];
+        load_raw<VEC>(rowp, base, len, x);
+#pragma unroll
+        for (int q = 0; q < kEpt / 4; ++q) {
+          const int32_t e = tile_pos(base, q, 0);
+          if (e < len) classify(x[q].x, e, 0, cut, rg, on_above, on_cand);
+          if (e + 1 < len) classify(x[q].y, e + 1, 0, cut, rg, on_above, on_cand);
+          if (e + 2 < len) classify(x[q].z, e + 2, 0, cut, rg, on_above, on_cand);
+          if (e + 3 < len) classify(x[q].w, e + 3, 0, cut, rg, on_above, on_cand);
+        }
+      } else {
+        load_pack<VEC>(rowp, base, len, hk);
+        extract(interest_mask(hk, cut.vlo), base, rowp, cut.vhi, rg, on_above, on_cand);
+      }
     }
   }
   merge_range(rg, sh);
@@ -1317,7 +1409,9 @@ static_assert(kHk * kBlock * 4 <= kListCap / 2 * 8, "a parked tile fits in half 
 static_assert(kBins * kHistCopies * 4 <= kListCap / 2 * 8, "histogram copies fit below a parked tile");
 
 // parked: this item's register tile is already in LDS (parked_tile).
-template <bool VEC>
+// STREAM: items longer than one register tile can occur (otherwise their code
+// is left out, which keeps it from weighing on the resident path's registers).
+template <bool VEC, bool STREAM>
 __device__ __forceinline__ void process_item(const SelectArgs& a, const WorkItem& w, Smem& sh, bool parked = false) {
   const int t = threadIdx.x;
   const int row = w.row;
@@ -1351,7 +1445,14 @@ __device__ __forceinline__ void process_item(const SelectArgs& a, const WorkItem
   }
   const float* rowp = a.scores + (int64_t)row * a.stride;
   const int32_t begin = w.begin, end = min(w.end, len);
-  const bool resident = end - begin <= kTile;
+  bool resident = end - begin <= kTile;
+  if constexpr (!STREAM) {
+    if (!resident) {   // excluded by the host's choice of variant; never silently
+      if (t == 0) atomicOr(a.status, TOPK_DEVICE_INTERNAL);
+      return;
+    }
+    resident = true;
+  }
   uint32_t hk[kHk];
   uint32_t* hc = reinterpret_cast<uint32_t*>(sh.list);   // free until the extraction
   hist_copies_clear(hc);
@@ -1366,9 +1467,18 @@ __device__ __forceinline__ void process_item(const SelectArgs& a, const WorkItem
     }
     hist_packed(hk, hc, begin, end);
   } else {
-    for (int32_t base = begin; base < end; base += kTile) {
-      load_pack<VEC>(rowp, base, end, hk);
-      hist_packed(hk, hc, base, end);
+    // Streamed in half tiles: the next half's loads are in flight while this
+    // one is binned.
+    constexpr int kHalf = kEpt / 8;   // dwordx4 per lane per step
+    constexpr int32_t kStep = kHalf * kBlock * 4;
+    float4 xa[kHalf];
+    load_vecs<VEC, kHalf>(rowp, begin, end, xa);
+    for (int32_t base = begin; base < end; base += kStep) {
+      float4 xb[kHalf];
+      if (base + kStep < end) load_vecs<VEC, kHalf>(rowp, base + kStep, end, xb);
+      hist_vecs<kHalf>(xa, hc, base, end);
+#pragma unroll
+      for (int q = 0; q < kHalf; ++q) xa[q] = xb[q];
     }
   }
   __syncthreads();
@@ -1405,18 +1515,26 @@ __device__ __forceinline__ int plan_here(const SelectArgs& a, Smem& sh) {
   const int t = threadIdx.x;
   const int R = a.num_rows;
   const int32_t len = t < R ? a.lengths[t] : 0;
-  const bool longer = t < R && len > a.k;
+  const bool longer = t < R && len > split_floor(plan_args_of(a));
   uint64_t mine = longer ? (uint64_t)len + (1ull << 40) : 0ull;   // lengths < 2^31, rows < 2^23
   mine = wave_sum_u64(mine);
-  if (lane() == 0) sh.pl_red[t >> 6] = mine;
+  const uint32_t tl = wave_sum_u32(longer ? (uint32_t)tiles_of(len) : 0u);
+  if (lane() == 0) {
+    sh.pl_red[t >> 6] = mine;
+    sh.pl_red2[t >> 6] = tl;
+  }
   __syncthreads();
   uint64_t packed = 0;
+  uint32_t tiles = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) packed += sh.pl_red[i];
+  for (int i = 0; i < kWaves; ++i) {
+    packed += sh.pl_red[i];
+    tiles += sh.pl_red2[i];
+  }
   const uint64_t total = packed & ((1ull << 40) - 1);
   const int32_t n_long = (int32_t)(packed >> 40);
   int64_t c;
-  const int g = t < R ? split_of(len, plan_args_of(a), total, n_long, &c) : 0;
+  const int g = t < R ? split_of(len, plan_args_of(a), total, n_long, tiles, &c) : 0;
   // One scan of three packed counts: split items (12 bits: at most the
   // grid, which the host keeps below 4096 for this path), split rows and
   // whole rows (10 bits each: at most kInKernelPlanRows).
@@ -1463,7 +1581,7 @@ __device__ __forceinline__ int plan_here(const SelectArgs& a, Smem& sh) {
   return fits ? num_items : -1;
 }
 
-template <bool VEC>
+template <bool VEC, bool STREAM>
 __global__ void __launch_bounds__(kBlock) topk_select_kernel(SelectArgs a) {
   __shared__ Smem sh;
   int num_items;
@@ -1490,9 +1608,11 @@ __global__ void __launch_bounds__(kBlock) topk_select_kernel(SelectArgs a) {
     // arguments and blockIdx)
     {
       const int32_t L = (int32_t)a.max_len;
-      const uint64_t total = L > a.k ? (uint64_t)L * (uint64_t)a.num_rows : 0ull;
+      const bool longer = L > split_floor(plan_args_of(a));
+      const uint64_t total = longer ? (uint64_t)L * (uint64_t)a.num_rows : 0ull;
       int64_t c;
-      const int g = split_of(L, plan_args_of(a), total, L > a.k ? a.num_rows : 0, &c);
+      const uint32_t tiles = longer ? (uint32_t)(tiles_of(L) * a.num_rows) : 0u;
+      const int g = split_of(L, plan_args_of(a), total, longer ? a.num_rows : 0, tiles, &c);
       const int B = (int)blockIdx.x;
       if (g > 1 && B < a.num_rows * g) {
         srow = B / g;
@@ -1528,7 +1648,7 @@ __global__ void __launch_bounds__(kBlock) topk_select_kernel(SelectArgs a) {
   for (int it = blockIdx.x; it < num_items; it += gridDim.x) {
     const WorkItem w = a.plan ? (it == (int)blockIdx.x ? first : a.items[it])
                               : sh.pl_items[(it - (int)blockIdx.x) / (int)gridDim.x];
-    process_item<VEC>(a, w, sh, parked && it == (int)blockIdx.x);
+    process_item<VEC, STREAM>(a, w, sh, parked && it == (int)blockIdx.x);
     __syncthreads();
   }
 }
@@ -1556,15 +1676,21 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
 
 // With events, they record the dispatch's own start and end (the same
 // interval a kernel trace reports), not the stream position around it.
-hipError_t launch_select(const SelectArgs& a, int grid, bool vec, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
-  if (start || stop) {
-    if (vec) hipExtLaunchKernelGGL(topk_select_kernel<true>, dim3(grid), dim3(kBlock), 0, s, start, stop, 0, a);
-    else hipExtLaunchKernelGGL(topk_select_kernel<false>, dim3(grid), dim3(kBlock), 0, s, start, stop, 0, a);
-  } else if (vec) {
-    hipLaunchKernelGGL(topk_select_kernel<true>, dim3(grid), dim3(kBlock), 0, s, a);
-  } else {
-    hipLaunchKernelGGL(topk_select_kernel<false>, dim3(grid), dim3(kBlock), 0, s, a);
-  }
+template <bool VEC, bool STREAM>
+void launch_select_t(const SelectArgs& a, int grid, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+  void (*kernel)(SelectArgs) = topk_select_kernel<VEC, STREAM>;
+  if (start || stop)
+    hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), 0, s, start, stop, 0, a);
+  else
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), 0, s, a);
+}
+
+hipError_t launch_select(const SelectArgs& a, int grid, bool vec, bool stream_items, hipStream_t s, hipEvent_t start,
+                         hipEvent_t stop) {
+  if (vec && stream_items) launch_select_t<true, true>(a, grid, s, start, stop);
+  else if (vec) launch_select_t<true, false>(a, grid, s, start, stop);
+  else if (stream_items) launch_select_t<false, true>(a, grid, s, start, stop);
+  else launch_select_t<false, false>(a, grid, s, start, stop);
   return hipGetLastError();
 }
 
@@ -1587,11 +1713,16 @@ hipError_t launch_debug_keys(const float* x, int64_t n, uint32_t* bin, uint32_t*
 
 hipError_t select_occupancy(int* per_cu) {
   int a = 0, b = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, (const void*)topk_select_kernel<true>, kBlock, 0);
-  if (e != hipSuccess) return e;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, (const void*)topk_select_kernel<false>, kBlock, 0);
-  if (e != hipSuccess) return e;
-  *per_cu = a < b ? a : b;
+  const void* kernels[4] = {(const void*)topk_select_kernel<true, true>, (const void*)topk_select_kernel<true, false>,
+                            (const void*)topk_select_kernel<false, true>, (const void*)topk_select_kernel<false, false>};
+  int best = 1 << 30;
+  for (const void* f : kernels) {
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, f, kBlock, 0);
+    if (e != hipSuccess) return e;
+    best = a < best ? a : best;
+  }
+  (void)b;
+  *per_cu = best;
   return hipSuccess;
 }
 

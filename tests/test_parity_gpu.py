@@ -218,3 +218,18 @@ def test_timed_entry_matches_and_times_the_kernel(workloads):
     kernel_ms, stream_ms = ks.elapsed_time(ke), ss.elapsed_time(se)
     _gpu.say(f"[timed] kernel {kernel_ms * 1e3:.1f} us, stream {stream_ms * 1e3:.1f} us")
     assert 0 < kernel_ms <= stream_ms * 1.01
+
+
+def test_mixed_long_rows_stay_register_resident():
+    """A batch whose row tile counts fit the grid: every chunk must fit one
+    register tile (the library then leaves the streamed-item code out), with
+    rows of very different lengths sharing the grid."""
+    st = synth.Stream(91)
+    lengths = np.array([1_000_000, 1_000_000, 40_000, 33_000, 2049, 0, 500_000], np.int32)
+    stride = 1_000_000
+    vals = synth._f32(st.normal(4096))
+    scores = vals[st.below(7 * stride, 4096)].reshape(7, stride)   # ties everywhere
+    bt = synth.page_permutation_tables(st, 1, stride // 64)
+    w = synth.Workload("mixed_long", np.ascontiguousarray(scores), lengths, bt, 0, 64, 2048, 91)
+    _gpu.say("[mixed] 7 rows up to 1M, lengths very uneven")
+    _gpu.assert_matches_oracle(w, _gpu.run_gpu(w, "auto", max_len=stride), "mixed long rows")
