@@ -233,3 +233,27 @@ def test_mixed_long_rows_stay_register_resident():
     w = synth.Workload("mixed_long", np.ascontiguousarray(scores), lengths, bt, 0, 64, 2048, 91)
     _gpu.say("[mixed] 7 rows up to 1M, lengths very uneven")
     _gpu.assert_matches_oracle(w, _gpu.run_gpu(w, "auto", max_len=stride), "mixed long rows")
+
+
+@pytest.mark.parametrize("kind", ["sorted", "all_equal", "random"])
+def test_split_rows_extreme_distributions(kind):
+    """Rows split across workgroups whose chunks fit the register tile, under
+    three score shapes: descending order (one chunk holds the whole top k),
+    all-equal scores (every element sits in the threshold bin, resolved only
+    by position) and random scores. Three calls in a row check that the
+    per-row cross-workgroup state is reset after each call."""
+    st = synth.Stream(300 + len(kind))
+    rows, n = 5, 100_000
+    if kind == "sorted":
+        scores = -np.sort(-synth._f32(st.normal(rows * n)).reshape(rows, n), axis=1)
+    elif kind == "all_equal":
+        scores = np.repeat(synth._f32(st.normal(rows))[:, None], n, axis=1)
+    else:
+        scores = synth._f32(st.normal(rows * n)).reshape(rows, n)
+    lengths = np.full(rows, n, np.int32)
+    bt = synth.page_permutation_tables(st, rows, (n + 63) // 64)
+    w = synth.Workload(f"split_{kind}", np.ascontiguousarray(scores, dtype=np.float32), lengths, bt,
+                       bt.shape[1], 64, 2048, 300)
+    _gpu.say(f"[split extreme] {kind}")
+    for got in _gpu.run_gpu(w, "auto", repeat=3):
+        _gpu.assert_matches_oracle(w, got, f"split {kind}")
