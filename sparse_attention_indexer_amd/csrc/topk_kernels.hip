@@ -465,7 +465,7 @@ __device__ __forceinline__ void load_pack(const float* rowp, int32_t base, int32
   pack_tile(x, base, end, hk);
 }
 
-// Histogram of a packed tile into kHistCopies interleaved copies of the
+// Histograms of a tile go into kHistCopies interleaved copies of the
 // 1,024 counters (bin r, copy c at word r * kHistCopies + c; lane l adds to
 // copy l % kHistCopies), so lanes that hit one hot bin in the same
 // instruction mostly land on different words and banks. When one bin takes
@@ -475,29 +475,42 @@ __device__ __forceinline__ void load_pack(const float* rowp, int32_t base, int32
 constexpr int kHistCopies = 16;
 static_assert(kBins * kHistCopies * 4 <= kListCap * 8, "histogram copies fit in the LDS list region");
 
-__device__ __forceinline__ void hist_packed(const uint32_t (&hk)[kHk], uint32_t* hc, int32_t base, int32_t end) {
+// Pack a tile (as pack_tile) and bin it into the copies in one pass over the
+// vectors, in load order, so the atomics of vector q go out while later
+// vectors are still arriving.
+__device__ __forceinline__ void pack_hist(const float4 (&x)[kEpt / 4], int32_t base, int32_t end,
+                                          uint32_t (&hk)[kHk], uint32_t* hc) {
   const uint32_t c = threadIdx.x & (kHistCopies - 1);
 #pragma unroll
   for (int q = 0; q < kEpt / 4; ++q) {
-    if (base + q * kBlock * 4 >= end) break;
-    const uint32_t p0 = hk[2 * q], p1 = hk[2 * q + 1];
-    const uint32_t r0 = (p0 >> 6) & 0x3FFu, r1 = p0 >> 22, r2 = (p1 >> 6) & 0x3FFu, r3 = p1 >> 22;
-    const uint32_t f = (uint32_t)__builtin_amdgcn_readfirstlane((int)r0);
-    const bool same = r0 == f && r1 == f && r2 == f && r3 == f;
-    if (__ballot(same) == ~0ull) {
-      if (lane() == 0) atomicAdd(&hc[f * kHistCopies + c], 256u);
-    } else {
-      atomicAdd(&hc[r0 * kHistCopies + c], 1u);
-      atomicAdd(&hc[r1 * kHistCopies + c], 1u);
-      atomicAdd(&hc[r2 * kHistCopies + c], 1u);
-      atomicAdd(&hc[r3 * kHistCopies + c], 1u);
+    const int32_t e = tile_pos(base, q, 0);
+    uint32_t p0 = to_half2(x[q].x, x[q].y), p1 = to_half2(x[q].z, x[q].w);
+    if (e + 4 > end) {  // tail vector: positions >= end become NaN
+      const int n = end - e;
+      p0 = n <= 0 ? kHalfNaN2 : (n == 1 ? (p0 & 0xFFFFu) | (kHalfNaN << 16) : p0);
+      p1 = n <= 2 ? kHalfNaN2 : (n == 3 ? (p1 & 0xFFFFu) | (kHalfNaN << 16) : p1);
+    }
+    hk[2 * q] = p0;
+    hk[2 * q + 1] = p1;
+    if (base + q * kBlock * 4 < end) {   // uniform
+      const uint32_t r0 = (p0 >> 6) & 0x3FFu, r1 = p0 >> 22, r2 = (p1 >> 6) & 0x3FFu, r3 = p1 >> 22;
+      const uint32_t f = (uint32_t)__builtin_amdgcn_readfirstlane((int)r0);
+      const bool same = r0 == f && r1 == f && r2 == f && r3 == f;
+      if (__ballot(same) == ~0ull) {
+        if (lane() == 0) atomicAdd(&hc[f * kHistCopies + c], 256u);
+      } else {
+        atomicAdd(&hc[r0 * kHistCopies + c], 1u);
+        atomicAdd(&hc[r1 * kHistCopies + c], 1u);
+        atomicAdd(&hc[r2 * kHistCopies + c], 1u);
+        atomicAdd(&hc[r3 * kHistCopies + c], 1u);
+      }
     }
   }
 }
 
 // N dwordx4 per lane at positions base + (u * kBlock + t) * 4 (vectors that
 // start at or past `end` are not read), and their histogram (same layout and
-// fast path as hist_packed; positions past `end` are NaN).
+// fast path as pack_hist; positions past `end` are NaN).
 template <bool VEC, int N>
 __device__ __forceinline__ void load_vecs(const float* rowp, int32_t base, int32_t end, float4 (&x)[N]) {
 #pragma unroll
@@ -562,15 +575,19 @@ __device__ __forceinline__ void hist_copies_sum(const uint32_t* hc, uint32_t* h)
   }
 }
 
-// Bit j set <=> element j lies in the threshold bin or above it.
+// Bit j set <=> element j lies in the threshold bin or above it. The words
+// are shifted in from the top element down, (m << 1) | bit: setting bit j
+// directly would need the constant 1 << j in a register for every j above
+// 6 (these instructions take no 32-bit literal), and the compiler keeps
+// such constants in registers for the whole kernel.
 __device__ __forceinline__ uint64_t interest_mask(const uint32_t (&hk)[kHk], _Float16 vlo) {
   uint32_t lo = 0, hi = 0;
 #pragma unroll
-  for (int i = 0; i < kHk / 2; ++i) {
-    lo |= (uint32_t)(half_lo(hk[i]) >= vlo) << (2 * i);
-    lo |= (uint32_t)(half_hi(hk[i]) >= vlo) << (2 * i + 1);
-    hi |= (uint32_t)(half_lo(hk[i + kHk / 2]) >= vlo) << (2 * i);
-    hi |= (uint32_t)(half_hi(hk[i + kHk / 2]) >= vlo) << (2 * i + 1);
+  for (int i = kHk / 2 - 1; i >= 0; --i) {
+    lo = (lo << 1) | (uint32_t)(half_hi(hk[i]) >= vlo);
+    lo = (lo << 1) | (uint32_t)(half_lo(hk[i]) >= vlo);
+    hi = (hi << 1) | (uint32_t)(half_hi(hk[i + kHk / 2]) >= vlo);
+    hi = (hi << 1) | (uint32_t)(half_lo(hk[i + kHk / 2]) >= vlo);
   }
   return ((uint64_t)hi << 32) | lo;
 }
@@ -1412,8 +1429,17 @@ static_assert(kBins * kHistCopies * 4 <= kListCap / 2 * 8, "histogram copies fit
 // STREAM: items longer than one register tile can occur (otherwise their code
 // is left out, which keeps it from weighing on the resident path's registers).
 template <bool VEC, bool STREAM>
-__device__ __forceinline__ void process_item(const SelectArgs& a, const WorkItem& w, Smem& sh, bool parked = false) {
+__device__ __forceinline__ void process_item(const SelectArgs& a, const WorkItem& item, Smem& sh, bool parked = false) {
   const int t = threadIdx.x;
+  // (every field is uniform: held in scalar registers)
+  WorkItem w;
+  w.row = (int32_t)uni((uint32_t)item.row);
+  w.begin = (int32_t)uni((uint32_t)item.begin);
+  w.end = (int32_t)uni((uint32_t)item.end);
+  w.group = (int32_t)uni((uint32_t)item.group);
+  w.gsize = (int32_t)uni((uint32_t)item.gsize);
+  w.len = (int32_t)uni((uint32_t)item.len);
+  w.pad[0] = w.pad[1] = 0;
   const int row = w.row;
   const int32_t len = w.len;   // planned from the same lengths (one dependent load fewer)
   if (len < 0 || (int64_t)len > a.max_len) {
@@ -1455,17 +1481,20 @@ __device__ __forceinline__ void process_item(const SelectArgs& a, const WorkItem
   }
   uint32_t hk[kHk];
   uint32_t* hc = reinterpret_cast<uint32_t*>(sh.list);   // free until the extraction
-  hist_copies_clear(hc);
-  __syncthreads();
+  if (!parked) {   // (a parked tile's histogram is already in the copies)
+    hist_copies_clear(hc);
+    __syncthreads();
+  }
   if (resident) {
     if (parked) {
       const uint32_t* pt = parked_tile(sh);
 #pragma unroll
       for (int i = 0; i < kHk; ++i) hk[i] = pt[i * kBlock + t];
     } else {
-      load_pack<VEC>(rowp, begin, end, hk);
+      float4 x[kEpt / 4];
+      load_raw<VEC>(rowp, begin, end, x);
+      pack_hist(x, begin, end, hk, hc);
     }
-    hist_packed(hk, hc, begin, end);
   } else {
     // Streamed in half tiles: the next half's loads are in flight while this
     // one is binned.
@@ -1585,13 +1614,12 @@ template <bool VEC, bool STREAM>
 __global__ void __launch_bounds__(kBlock) topk_select_kernel(SelectArgs a) {
   __shared__ Smem sh;
   int num_items;
-  WorkItem first{};
   bool parked = false;
   if (a.plan) {
-    // The first item is fetched together with the header (the plan buffer
-    // always holds at least gridDim.x items, so the read stays in bounds; the
-    // item is used only if the header says it exists).
-    first = a.items[blockIdx.x];
+    // The first item is fetched together with the header and staged in LDS
+    // (the plan buffer always holds at least gridDim.x items, so the read
+    // stays in bounds; the item is used only if the header says it exists).
+    if (threadIdx.x == 0) sh.pl_items[0] = a.items[blockIdx.x];
     const PlanHeader h = *a.plan;
     if (h.magic != kPlanMagic || h.k != a.k || h.grid != (int)gridDim.x || h.num_rows > a.num_rows) {
       if (threadIdx.x == 0 && blockIdx.x == 0) atomicOr(a.status, TOPK_DEVICE_PLAN_MISMATCH);
@@ -1625,20 +1653,23 @@ __global__ void __launch_bounds__(kBlock) topk_select_kernel(SelectArgs a) {
       if (srow >= 0 && send - sbeg <= kTile) load_raw<VEC>(a.scores + (int64_t)srow * a.stride, sbeg, send, x);
       else srow = -1;
     }
+    // (the barriers of the planning order this clear before any histogram add)
+    if (srow >= 0) hist_copies_clear(reinterpret_cast<uint32_t*>(sh.list));
     num_items = plan_here(a, sh);
     if (num_items < 0) {
       if (threadIdx.x == 0 && blockIdx.x == 0) atomicOr(a.status, TOPK_DEVICE_PLAN_MISMATCH);
       return;
     }
     // Park the tile if the real plan gave the guessed chunk (the same row and
-    // start, ending no later; positions past the real end become NaN).
+    // start, ending no later; positions past the real end become NaN),
+    // binning each vector as it arrives.
     if ((int)blockIdx.x < num_items && srow >= 0) {
       const WorkItem w0 = sh.pl_items[0];
       const int32_t end0 = min(w0.end, w0.len);
       parked = w0.row == srow && w0.begin == sbeg && end0 <= send && w0.len > a.k && (int64_t)w0.len <= a.max_len;
       if (parked) {
         uint32_t hk[kHk];
-        pack_tile(x, sbeg, end0, hk);
+        pack_hist(x, sbeg, end0, hk, reinterpret_cast<uint32_t*>(sh.list));
         uint32_t* pt = parked_tile(sh);
 #pragma unroll
         for (int i = 0; i < kHk; ++i) pt[i * kBlock + threadIdx.x] = hk[i];
@@ -1646,9 +1677,16 @@ __global__ void __launch_bounds__(kBlock) topk_select_kernel(SelectArgs a) {
     }
   }
   for (int it = blockIdx.x; it < num_items; it += gridDim.x) {
-    const WorkItem w = a.plan ? (it == (int)blockIdx.x ? first : a.items[it])
-                              : sh.pl_items[(it - (int)blockIdx.x) / (int)gridDim.x];
-    process_item<VEC, STREAM>(a, w, sh, parked && it == (int)blockIdx.x);
+    // Items are read from LDS: a plan-buffer item is staged in slot 0 (the
+    // barrier after the previous item keeps it from being overwritten early).
+    int slot = 0;
+    if (a.plan) {
+      if (threadIdx.x == 0 && it != (int)blockIdx.x) sh.pl_items[0] = a.items[it];
+      __syncthreads();
+    } else {
+      slot = (it - (int)blockIdx.x) / (int)gridDim.x;
+    }
+    process_item<VEC, STREAM>(a, sh.pl_items[slot], sh, parked && it == (int)blockIdx.x);
     __syncthreads();
   }
 }

@@ -12,7 +12,8 @@ namespace satopk {
 // scores of a register-resident tile as packed FP16 (kEpt / 4 dwordx4 loads
 // in flight per lane, 128 KB per CU).
 constexpr int kBlock = 512;
-constexpr int kWaves = kBlock / 64;
+constexpr int kWave = 64;                // lanes per wavefront
+constexpr int kWaves = kBlock / kWave;
 constexpr int kEpt = 64;
 constexpr int kTile = kBlock * kEpt;          // 32,768 scores = 128 KB per tile
 
