@@ -7,6 +7,7 @@
 
 #include "sparse_topk.h"
 #include "topk_layout.hpp"
+#include "topk_plan.hpp"
 
 static_assert(satopk::kInKernelPlanRows == TOPK_IN_KERNEL_PLAN_ROWS, "header and kernels agree");
 static_assert(satopk::kInKernelPlanRows <= satopk::kBlock, "one row per thread");
@@ -214,6 +215,29 @@ topk_status select_impl(const topk_config* cfg, const void* plan, const float* s
   a.status = (int32_t*)workspace;
   a.max_len = cfg->max_len;
   a.spin_limit = kDefaultSpinLimit;
+  // The selection kernel starts loading its tile before the lengths arrive,
+  // guessing that every row has max_len scores; the guess is the planner's
+  // own split of such a batch.
+  a.guess_groups = 1;
+  a.guess_chunk = cfg->max_len;
+  if (here) {
+    PlanArgs p{};
+    p.num_rows = num_rows;
+    p.k = cfg->k;
+    p.grid = s.grid;
+    p.max_groups = s.max_groups;
+    p.force_path = a.force_path;
+    p.wg_per_row = a.wg_per_row;
+    p.min_chunk = a.min_chunk;
+    p.max_len = cfg->max_len;
+    const int32_t L = (int32_t)cfg->max_len;
+    const bool longer = L > split_floor(p);
+    const uint64_t total = longer ? (uint64_t)L * (uint64_t)num_rows : 0ull;
+    const uint32_t tiles = longer ? (uint32_t)(tiles_of(L) * num_rows) : 0u;
+    int64_t c = L;
+    a.guess_groups = split_of(L, p, total, longer ? num_rows : 0, tiles, &c);
+    a.guess_chunk = c;
+  }
   const bool vec = ((uintptr_t)scores % 16 == 0) && (score_row_stride % 4 == 0);
   return launch_select(a, s.grid, vec, items_may_stream(cfg, s), (hipStream_t)stream, (hipEvent_t)start_event,
                        (hipEvent_t)stop_event) ==

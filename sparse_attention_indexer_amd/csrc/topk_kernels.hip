@@ -25,6 +25,7 @@
 #include "sparse_topk.h"
 #include "topk_device.hpp"
 #include "topk_layout.hpp"
+#include "topk_plan.hpp"
 
 namespace satopk {
 
@@ -32,61 +33,6 @@ namespace satopk {
 // Planning kernel: one workgroup reads the device lengths and writes the plan.
 // ---------------------------------------------------------------------------
 constexpr int kPlanBlock = 256;
-
-__device__ __forceinline__ int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
-__device__ __forceinline__ int64_t round_up64(int64_t a, int64_t b) { return ceil_div64(a, b) * b; }
-
-// Workgroups a row of `len` scores gets (1 = the row stays whole).
-//  - fixed: a fixed group size for every row longer than k;
-//  - force_split: at least 2, the grid's remaining workgroups shared in
-//    proportion to length (at most 2 per row + the rest: fits one round);
-//  - otherwise: rows that fit one register tile stay whole; each takes one
-//    item, and the rest of the grid (the budget) goes to the longer rows.
-//    A longer row first gets one workgroup per register tile it spans (so
-//    every chunk stays register-resident), when those add up to no more than
-//    the budget (`tiles` is their sum over the batch); the rest of the budget
-//    is shared in proportion to length, floor-rounded, so all items fit one
-//    round of the persistent grid, with no chunk shorter than min_chunk.
-// `total` and `n_long` sum over the rows this mode splits: longer than one
-// tile by default, longer than k under a forced split or fixed group size.
-// The chunk is then aligned to kChunkAlign, which can only lower the count.
-__device__ __forceinline__ int64_t tiles_of(int32_t len) { return len > kTile ? ceil_div64(len, kTile) : 0; }
-__device__ __forceinline__ int32_t split_floor(const PlanArgs& a) {
-  return (a.force_path == TOPK_PATH_AUTO && a.wg_per_row <= 0) ? max(kTile, a.k) : a.k;
-}
-
-__device__ __forceinline__ int split_of(int32_t len, const PlanArgs& a, uint64_t total, int32_t n_long,
-                                        uint32_t tiles, int64_t* chunk_out) {
-  *chunk_out = len;
-  if (len <= a.k || total == 0) return 1;
-  int64_t g;
-  if (a.wg_per_row > 0) {
-    g = a.wg_per_row;
-  } else if (a.force_path == TOPK_PATH_MULTI) {
-    const int64_t spare = (int64_t)a.grid - 2 * (int64_t)n_long;
-    g = 2 + (spare > 0 ? (int64_t)((uint64_t)spare * (uint64_t)len / total) : 0);
-  } else if (a.force_path == TOPK_PATH_REGISTER || a.force_path == TOPK_PATH_SINGLE) {
-    return 1;
-  } else {
-    // A row that fits one workgroup's register tile stays whole: one pass
-    // with no cross-workgroup exchange beats any split of it.
-    if (len <= kTile) return 1;
-    const int64_t budget = (int64_t)a.grid - ((int64_t)a.num_rows - n_long);
-    if (budget >= (int64_t)tiles)
-      g = tiles_of(len) + (int64_t)((uint64_t)(budget - (int64_t)tiles) * (uint64_t)len / total);
-    else
-      g = (int64_t)((uint64_t)a.grid * (uint64_t)len / total);
-    const int64_t min_chunk = a.min_chunk > 0 ? a.min_chunk : kDefaultMinChunk;
-    const int64_t by_min = len / min_chunk;
-    if (g > by_min) g = by_min;
-  }
-  if (g < 2) return 1;
-  const int64_t c = round_up64(ceil_div64(len, g), kChunkAlign);
-  g = ceil_div64(len, c);
-  if (g < 2) return 1;
-  *chunk_out = c;
-  return (int)g;
-}
 
 constexpr int kPlanWaves = kPlanBlock / 64;
 
@@ -1271,7 +1217,9 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
       }
     }
   }
-  if (t == 0) {
+  // (polled from the last wave, which holds no pre-read entries unless
+  // there are more than 448: its loads do not wait behind theirs)
+  if (t == kBlock - kWave) {
     uint32_t spins = 0, ok = 1;
     while (ld_agent(&g->arrive) < G) {
       __builtin_amdgcn_s_sleep(1);
@@ -1636,11 +1584,8 @@ __global__ void __launch_bounds__(kBlock) topk_select_kernel(SelectArgs a) {
     // arguments and blockIdx)
     {
       const int32_t L = (int32_t)a.max_len;
-      const bool longer = L > split_floor(plan_args_of(a));
-      const uint64_t total = longer ? (uint64_t)L * (uint64_t)a.num_rows : 0ull;
-      int64_t c;
-      const uint32_t tiles = longer ? (uint32_t)(tiles_of(L) * a.num_rows) : 0u;
-      const int g = split_of(L, plan_args_of(a), total, longer ? a.num_rows : 0, tiles, &c);
+      const int g = a.guess_groups;       // the planner's split of a max_len row,
+      const int64_t c = a.guess_chunk;    // worked out by the host
       const int B = (int)blockIdx.x;
       if (g > 1 && B < a.num_rows * g) {
         srow = B / g;

@@ -129,6 +129,8 @@ struct SelectArgs {
   int32_t* status;
   int64_t max_len;
   uint32_t spin_limit;
+  int32_t guess_groups;     // in-kernel planning: the split of a max_len row when every
+  int64_t guess_chunk;      // row has max_len scores (groups per row, chunk length)
 };
 
 }  // namespace satopk
