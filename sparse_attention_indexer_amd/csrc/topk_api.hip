@@ -14,8 +14,8 @@ static_assert(satopk::kInKernelPlanRows <= satopk::kBlock, "one row per thread")
 
 namespace satopk {
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
-hipError_t launch_select(const SelectArgs& a, int grid, bool vec, bool stream_items, hipStream_t s, hipEvent_t start,
-                         hipEvent_t stop);
+hipError_t launch_select(const SelectArgs& a, int grid, bool vec, bool stream_items, bool overlap, hipStream_t s,
+                         hipEvent_t start, hipEvent_t stop);
 hipError_t launch_fill(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_debug_keys(const float* x, int64_t n, uint32_t* bin, uint32_t* k32, hipStream_t s);
 hipError_t select_occupancy(int* per_cu);
@@ -110,12 +110,16 @@ topk_status sizing(const topk_config* cfg, Sizing* s) {
 // Whether some work item can exceed one register tile. With the planner's
 // defaults every row longer than a tile gets at least one workgroup per tile
 // when the rows' tile counts fit the grid, which max_rows * ceil(max_len /
-// tile) bounds; forced paths, fixed group sizes and large minimum chunks can
-// still produce longer items.
+// tile) bounds. Forced paths and fixed group sizes can still produce longer
+// items, and so can a minimum chunk above half a tile: the cap of
+// floor(len / min_chunk) workgroups can then fall below ceil(len / tile)
+// (at len = 80,000 and min_chunk = 32,768: 2 workgroups, chunks of 40,192).
+// At or below half a tile, floor(len / min_chunk) >= floor(2 len / tile)
+// >= ceil(len / tile) for every len above a tile.
 bool items_may_stream(const topk_config* cfg, const Sizing& s) {
   if (cfg->max_len <= kTile) return false;
   if (cfg->force_path == TOPK_PATH_REGISTER) return false;   // max_len <= kTile is enforced
-  if (cfg->force_path != TOPK_PATH_AUTO || cfg->wg_per_row > 0 || cfg->min_chunk > kTile) return true;
+  if (cfg->force_path != TOPK_PATH_AUTO || cfg->wg_per_row > 0 || cfg->min_chunk > kTile / 2) return true;
   const int64_t tiles = (cfg->max_len + kTile - 1) / kTile;
   return (int64_t)cfg->max_rows * tiles > s.grid;
 }
@@ -239,7 +243,11 @@ topk_status select_impl(const topk_config* cfg, const void* plan, const float* s
     a.guess_chunk = c;
   }
   const bool vec = ((uintptr_t)scores % 16 == 0) && (score_row_stride % 4 == 0);
-  return launch_select(a, s.grid, vec, items_may_stream(cfg, s), (hipStream_t)stream, (hipEvent_t)start_event,
+  // The planning overlaps the guessed tile's loads when that tile is at least
+  // half a tile long.
+  const int64_t guess_len = a.guess_groups > 1 ? a.guess_chunk : cfg->max_len;
+  const bool overlap = here && guess_len >= kTile / 2 && guess_len <= kTile;
+  return launch_select(a, s.grid, vec, items_may_stream(cfg, s), overlap, (hipStream_t)stream, (hipEvent_t)start_event,
                        (hipEvent_t)stop_event) ==
                  hipSuccess
              ? TOPK_OK

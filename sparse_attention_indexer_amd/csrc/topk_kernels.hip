@@ -387,6 +387,35 @@ __device__ __forceinline__ void load_raw(const float* rowp, int32_t base, int32_
   }
 }
 
+// The same loads through a buffer resource that covers [base, end) of the
+// row (at most one tile): positions at or past `end` read as zero without a
+// memory access and without a branch, so every load is issued
+// unconditionally. (A load under a per-lane branch lets the compiler move
+// its first use into the branch, where the wait for it also waits for every
+// earlier load; the speculative tile load must not wait before the planning
+// that overlaps it.) Consumers mask positions past `end` as for load_raw.
+constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
+
+template <bool VEC>
+__device__ __forceinline__ void load_raw_buffer(const float* rowp, int32_t base, int32_t end,
+                                                float4 (&x)[kEpt / 4]) {
+  const int32_t n = end > base ? min(end - base, (int32_t)kTile) : 0;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(rowp) + base, (short)0, n * 4, kBufferFlags);
+#pragma unroll
+  for (int q = 0; q < kEpt / 4; ++q) {
+    const int32_t off = (q * kBlock + (int)threadIdx.x) * 16;   // bytes from `base`
+    if constexpr (VEC) {
+      x[q] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    } else {
+      x[q].x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+      x[q].y = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4, 0, 0));
+      x[q].z = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off + 8, 0, 0));
+      x[q].w = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off + 12, 0, 0));
+    }
+  }
+}
+
 // Raw loads -> packed FP16 tile; positions at or past `end` become NaN.
 __device__ __forceinline__ void pack_tile(const float4 (&x)[kEpt / 4], int32_t base, int32_t end,
                                           uint32_t (&hk)[kHk]) {
@@ -1488,10 +1517,9 @@ __device__ __forceinline__ PlanArgs plan_args_of(const SelectArgs& a) {
   return p;
 }
 
-__device__ __forceinline__ int plan_here(const SelectArgs& a, Smem& sh) {
+__device__ __forceinline__ int plan_here(const SelectArgs& a, Smem& sh, int32_t len) {
   const int t = threadIdx.x;
   const int R = a.num_rows;
-  const int32_t len = t < R ? a.lengths[t] : 0;
   const bool longer = t < R && len > split_floor(plan_args_of(a));
   uint64_t mine = longer ? (uint64_t)len + (1ull << 40) : 0ull;   // lengths < 2^31, rows < 2^23
   mine = wave_sum_u64(mine);
@@ -1558,7 +1586,87 @@ __device__ __forceinline__ int plan_here(const SelectArgs& a, Smem& sh) {
   return fits ? num_items : -1;
 }
 
-template <bool VEC, bool STREAM>
+// In-kernel planning with a guessed first tile. Each workgroup starts
+// loading the tile it would get if every row had max_len scores, before the
+// lengths arrive, then plans; the loads are used when the real plan gives the
+// same chunk (every batch of equal lengths), and the tile is then packed,
+// binned and parked in LDS. Returns whether it was; num_items as plan_here.
+// OVERLAP: the lengths are requested first and the tile goes through a
+// buffer resource (no per-lane branches), so the planning waits for the
+// lengths only and runs while the tile arrives. Without it, the tile is
+// converted as it arrives and the planning follows.
+template <bool VEC, bool OVERLAP>
+__device__ __forceinline__ bool guess_and_plan(const SelectArgs& a, Smem& sh, int& num_items) {
+  int32_t len_t = 0;
+  if constexpr (OVERLAP) {
+    // (loads complete in order: waiting for the length does not wait for the tile)
+    len_t = (int)threadIdx.x < a.num_rows ? a.lengths[threadIdx.x] : 0;
+    asm volatile("" ::: "memory");
+  }
+  float4 x[kEpt / 4];
+  int32_t srow = -1, sbeg = 0, send = 0;
+  // (uniform across the workgroup: every value below derives from kernel
+  // arguments and blockIdx)
+  {
+    const int32_t L = (int32_t)a.max_len;
+    const int g = a.guess_groups;       // the planner's split of a max_len row,
+    const int64_t c = a.guess_chunk;    // worked out by the host
+    const int B = (int)blockIdx.x;
+    if (g > 1 && B < a.num_rows * g) {
+      srow = B / g;
+      sbeg = (int32_t)((B % g) * c);
+      send = (int32_t)min((int64_t)sbeg + c, (int64_t)L);
+    } else if (g <= 1 && L > a.k && B < a.num_rows) {
+      srow = B;
+      send = L;
+    }
+    if constexpr (OVERLAP) {
+      if (srow < 0 || send - sbeg > kTile) {   // no guess: nothing is read
+        srow = -1;
+        sbeg = send = 0;
+      }
+      load_raw_buffer<VEC>(a.scores + (int64_t)max(srow, 0) * a.stride, sbeg, send, x);
+    } else {
+      if (srow >= 0 && send - sbeg <= kTile) load_raw<VEC>(a.scores + (int64_t)srow * a.stride, sbeg, send, x);
+      else srow = -1;
+    }
+  }
+  // (the barriers of the planning order this clear before any histogram add)
+  if (srow >= 0) hist_copies_clear(reinterpret_cast<uint32_t*>(sh.list));
+  if constexpr (!OVERLAP) len_t = (int)threadIdx.x < a.num_rows ? a.lengths[threadIdx.x] : 0;
+  num_items = plan_here(a, sh, len_t);
+  if constexpr (OVERLAP) {
+    // Keep the tile's first use here: the compiler would otherwise convert
+    // each vector as it arrives, ahead of the planning, and the planning
+    // would then wait for the whole tile.
+#pragma unroll
+    for (int q = 0; q < kEpt / 4; ++q) asm volatile("" : "+v"(x[q].x), "+v"(x[q].y), "+v"(x[q].z), "+v"(x[q].w));
+  }
+  if (num_items < 0) return false;
+  // Park the tile if the real plan gave the guessed chunk (the same row and
+  // start, ending no later; positions past the real end become NaN),
+  // binning each vector as it arrives.
+  bool parked = false;
+  if ((int)blockIdx.x < num_items && srow >= 0) {
+    const WorkItem w0 = sh.pl_items[0];
+    const int32_t end0 = min(w0.end, w0.len);
+    parked = w0.row == srow && w0.begin == sbeg && end0 <= send && w0.len > a.k && (int64_t)w0.len <= a.max_len;
+    if (parked) {
+      uint32_t hk[kHk];
+      pack_hist(x, sbeg, end0, hk, reinterpret_cast<uint32_t*>(sh.list));
+      uint32_t* pt = parked_tile(sh);
+#pragma unroll
+      for (int i = 0; i < kHk; ++i) pt[i * kBlock + threadIdx.x] = hk[i];
+    }
+  }
+  return parked;
+}
+
+// OVERLAP: the in-kernel planning overlaps the guessed tile's loads (chosen
+// by the host for guessed tiles of at least half a tile; smaller ones arrive
+// about as soon as the lengths do, and skipping their empty vector groups
+// is worth more than the overlap).
+template <bool VEC, bool STREAM, bool OVERLAP>
 __global__ void __launch_bounds__(kBlock) topk_select_kernel(SelectArgs a) {
   __shared__ Smem sh;
   int num_items;
@@ -1575,50 +1683,10 @@ __global__ void __launch_bounds__(kBlock) topk_select_kernel(SelectArgs a) {
     }
     num_items = h.num_items;
   } else {
-    // Start loading this workgroup's tile as planned for a batch whose rows
-    // all have max_len scores, before the lengths arrive; the loads are used
-    // when the real plan gives the same chunk (every batch of equal lengths).
-    float4 x[kEpt / 4];
-    int32_t srow = -1, sbeg = 0, send = 0;
-    // (uniform across the workgroup: every value below derives from kernel
-    // arguments and blockIdx)
-    {
-      const int32_t L = (int32_t)a.max_len;
-      const int g = a.guess_groups;       // the planner's split of a max_len row,
-      const int64_t c = a.guess_chunk;    // worked out by the host
-      const int B = (int)blockIdx.x;
-      if (g > 1 && B < a.num_rows * g) {
-        srow = B / g;
-        sbeg = (int32_t)((B % g) * c);
-        send = (int32_t)min((int64_t)sbeg + c, (int64_t)L);
-      } else if (g <= 1 && L > a.k && B < a.num_rows) {
-        srow = B;
-        send = L;
-      }
-      if (srow >= 0 && send - sbeg <= kTile) load_raw<VEC>(a.scores + (int64_t)srow * a.stride, sbeg, send, x);
-      else srow = -1;
-    }
-    // (the barriers of the planning order this clear before any histogram add)
-    if (srow >= 0) hist_copies_clear(reinterpret_cast<uint32_t*>(sh.list));
-    num_items = plan_here(a, sh);
+    parked = guess_and_plan<VEC, OVERLAP>(a, sh, num_items);
     if (num_items < 0) {
       if (threadIdx.x == 0 && blockIdx.x == 0) atomicOr(a.status, TOPK_DEVICE_PLAN_MISMATCH);
       return;
-    }
-    // Park the tile if the real plan gave the guessed chunk (the same row and
-    // start, ending no later; positions past the real end become NaN),
-    // binning each vector as it arrives.
-    if ((int)blockIdx.x < num_items && srow >= 0) {
-      const WorkItem w0 = sh.pl_items[0];
-      const int32_t end0 = min(w0.end, w0.len);
-      parked = w0.row == srow && w0.begin == sbeg && end0 <= send && w0.len > a.k && (int64_t)w0.len <= a.max_len;
-      if (parked) {
-        uint32_t hk[kHk];
-        pack_hist(x, sbeg, end0, hk, reinterpret_cast<uint32_t*>(sh.list));
-        uint32_t* pt = parked_tile(sh);
-#pragma unroll
-        for (int i = 0; i < kHk; ++i) pt[i * kBlock + threadIdx.x] = hk[i];
-      }
     }
   }
   for (int it = blockIdx.x; it < num_items; it += gridDim.x) {
@@ -1659,21 +1727,28 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
 
 // With events, they record the dispatch's own start and end (the same
 // interval a kernel trace reports), not the stream position around it.
-template <bool VEC, bool STREAM>
+template <bool VEC, bool STREAM, bool OVERLAP>
 void launch_select_t(const SelectArgs& a, int grid, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
-  void (*kernel)(SelectArgs) = topk_select_kernel<VEC, STREAM>;
+  void (*kernel)(SelectArgs) = topk_select_kernel<VEC, STREAM, OVERLAP>;
   if (start || stop)
     hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), 0, s, start, stop, 0, a);
   else
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), 0, s, a);
 }
 
-hipError_t launch_select(const SelectArgs& a, int grid, bool vec, bool stream_items, hipStream_t s, hipEvent_t start,
-                         hipEvent_t stop) {
-  if (vec && stream_items) launch_select_t<true, true>(a, grid, s, start, stop);
-  else if (vec) launch_select_t<true, false>(a, grid, s, start, stop);
-  else if (stream_items) launch_select_t<false, true>(a, grid, s, start, stop);
-  else launch_select_t<false, false>(a, grid, s, start, stop);
+hipError_t launch_select(const SelectArgs& a, int grid, bool vec, bool stream_items, bool overlap, hipStream_t s,
+                         hipEvent_t start, hipEvent_t stop) {
+  if (vec && stream_items) {
+    if (overlap) launch_select_t<true, true, true>(a, grid, s, start, stop);
+    else launch_select_t<true, true, false>(a, grid, s, start, stop);
+  } else if (vec) {
+    if (overlap) launch_select_t<true, false, true>(a, grid, s, start, stop);
+    else launch_select_t<true, false, false>(a, grid, s, start, stop);
+  } else if (stream_items) {
+    launch_select_t<false, true, false>(a, grid, s, start, stop);
+  } else {
+    launch_select_t<false, false, false>(a, grid, s, start, stop);
+  }
   return hipGetLastError();
 }
 
@@ -1696,8 +1771,12 @@ hipError_t launch_debug_keys(const float* x, int64_t n, uint32_t* bin, uint32_t*
 
 hipError_t select_occupancy(int* per_cu) {
   int a = 0, b = 0;
-  const void* kernels[4] = {(const void*)topk_select_kernel<true, true>, (const void*)topk_select_kernel<true, false>,
-                            (const void*)topk_select_kernel<false, true>, (const void*)topk_select_kernel<false, false>};
+  const void* kernels[6] = {(const void*)topk_select_kernel<true, true, false>,
+                            (const void*)topk_select_kernel<true, false, false>,
+                            (const void*)topk_select_kernel<true, true, true>,
+                            (const void*)topk_select_kernel<true, false, true>,
+                            (const void*)topk_select_kernel<false, true, false>,
+                            (const void*)topk_select_kernel<false, false, false>};
   int best = 1 << 30;
   for (const void* f : kernels) {
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, f, kBlock, 0);

@@ -30,6 +30,8 @@ def workloads():
 CONFIG_CASES = [
     (1, "auto", {}), (1, "register", {}), (1, "single", {}), (1, "multi", {}), (1, "multi", {"wg_per_row": 4}),
     (2, "auto", {}), (2, "single", {}), (2, "multi", {"wg_per_row": 8}), (2, "multi", {"wg_per_row": 36}),
+    # minimum chunks above half a tile: the chunks then exceed one tile
+    (2, "auto", {"min_chunk": 32768}), (2, "auto", {"min_chunk": 20000}), (4, "auto", {"min_chunk": 30000}),
     (3, "auto", {}), (3, "single", {}), (3, "multi", {"cand_capacity": 64}),
     (4, "auto", {}), (4, "single", {}), (4, "multi", {}),
     (5, "auto", {}), (5, "single", {}),
