@@ -259,3 +259,18 @@ def test_split_rows_extreme_distributions(kind):
     _gpu.say(f"[split extreme] {kind}")
     for got in _gpu.run_gpu(w, "auto", repeat=3):
         _gpu.assert_matches_oracle(w, got, f"split {kind}")
+
+
+@pytest.mark.parametrize("max_len,exact,alphabet", [
+    (16_384, True, 0), (20_000, True, 0), (32_768, True, 97), (30_000, False, 0),   # whole rows
+    (70_000, True, 0), (140_000, True, 11), (100_000, False, 0),                    # split rows
+], ids=["16k", "20k", "32k-ties", "30k-ragged", "70k", "140k-ties", "100k-ragged"])
+def test_guessed_tile_paths(max_len, exact, alphabet):
+    """Batches planned in the kernel whose guessed first tile is at least half
+    a tile long (its loads then overlap the planning) or shorter, whole and
+    split rows, equal lengths (the guess holds) and ragged ones (it mostly
+    does not), with junk past every valid prefix."""
+    w = synth.random_case(700 + max_len % 997, 9, max_len, exact_len=exact, alphabet=alphabet)
+    _gpu.say(f"[guess] 9 rows, max_len {max_len}, exact {exact}, alphabet {alphabet}")
+    for got in _gpu.run_gpu(w, "auto", repeat=2):
+        _gpu.assert_matches_oracle(w, got, f"guessed tile {max_len}")
