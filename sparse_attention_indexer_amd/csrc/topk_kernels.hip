@@ -1202,16 +1202,28 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
     find_threshold_raw(sh.lhist, k, sh.scratch, sh.res);
     bloc = uni(sh.res[0]);
   }
+  // The scores of the chunk that no merged bin counts go to g->arrive, so the
+  // merged bins and that count add up to the row length once every
+  // workgroup's atomics have landed: there is no separate arrival (and no
+  // wait for the atomics before it).
+  uint32_t merged = 0;
   for (int r = t; r < kBins; r += kBlock) {
     const uint32_t h = sh.lhist[r];
     const uint32_t b = bin_of_raw((uint32_t)r);
-    if (h && b >= bloc && b >= kFirstBin && b <= kLastBin)
+    if (h && b >= bloc && b >= kFirstBin && b <= kLastBin) {
       __hip_atomic_fetch_add(&g->hist[r], h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      merged += h;
+    }
   }
-  drain_memory();
-  __syncthreads();
-  if (t == 0) __hip_atomic_fetch_add(&g->arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // While the other workgroups arrive: list the positions at or above the
+  {
+    uint32_t tot_merged;
+    block_exclusive_add(merged, sh.scratch, &tot_merged);
+    if (t == 0) {
+      const uint32_t chunk = end > begin ? (uint32_t)(end - begin) : 0u;
+      __hip_atomic_fetch_add(&g->arrive, chunk - tot_merged, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  // While the other workgroups merge: list the positions at or above the
   // local k-th bin and start reading their scores and block-table entries.
   uint32_t* pre = reinterpret_cast<uint32_t*>(sh.list + kStageCap);
   float pv[kPreRegs];
@@ -1246,24 +1258,33 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
       }
     }
   }
-  // (polled from the last wave, which holds no pre-read entries unless
-  // there are more than 448: its loads do not wait behind theirs)
-  if (t == kBlock - kWave) {
-    uint32_t spins = 0, ok = 1;
-    while (ld_agent(&g->arrive) < G) {
+  // Read the merged bins and the rest count until they add up to the row
+  // length. Every contribution is a non-negative add, so each value read is
+  // at most its final value; a read that sums to the final total therefore
+  // read every final value: a consistent snapshot of the merge.
+  {
+    static_assert(kBins == 2 * kBlock, "two bins per lane");
+    uint32_t spins = 0;
+    bool ok = true;
+    for (;;) {
+      const uint32_t h0 = ld_agent(&g->hist[t]), h1 = ld_agent(&g->hist[t + kBlock]);
+      const uint32_t rest = t == 0 ? ld_agent(&g->arrive) : 0u;
+      sh.rhist[t] = h0;
+      sh.rhist[t + kBlock] = h1;
+      uint32_t tot;
+      block_exclusive_add(h0 + h1 + rest, sh.scratch, &tot);
+      if (uni(tot) == (uint32_t)len) break;
       __builtin_amdgcn_s_sleep(1);
       if (++spins > a.spin_limit) {
-        ok = 0;
+        ok = false;
         break;
       }
     }
-    if (!ok) atomicOr(a.status, TOPK_DEVICE_SPIN_TIMEOUT);
-    sh.flag = ok;
+    if (!ok) {
+      if (t == 0) atomicOr(a.status, TOPK_DEVICE_SPIN_TIMEOUT);
+      return;
+    }
   }
-  __syncthreads();
-  if (!uni(sh.flag)) return;
-  for (int r = t; r < kBins; r += kBlock) sh.rhist[r] = ld_agent(&g->hist[r]);
-  __syncthreads();
   // Bins at or above the largest chunk threshold are complete, and the row's
   // threshold bin lies there, so the scan from the top is exact. Not found
   // only with NaN inputs; the workgroup then skips its emission but still

@@ -61,7 +61,7 @@ static_assert(sizeof(WorkItem) == 32, "work item is 32 bytes");
 // Cross-workgroup state of one split row. Left zeroed after every use.
 struct GroupState {
   uint32_t hist[kBins];   // merged 1,024-bin histogram
-  uint32_t arrive;        // workgroups that merged their histogram
+  uint32_t arrive;        // scores of the row that no merged bin counts
   uint32_t emit;          // output cursor for scores above the threshold bin
   uint32_t cand;          // cursor into this row's candidate buffer
   uint32_t done;          // workgroups that finished emission
