@@ -321,10 +321,28 @@ struct RowOut {
     return ok ? store_page(pos, i, page(i)) : false;
   }
 
-  // Whole workgroup; staged outputs [from, to).
+  // Whole workgroup; staged outputs [from, to), to <= k <= kMaxK. Each lane
+  // takes up to kFlushPer outputs and has all their block-table loads in
+  // flight before the first store (one round trip rather than one per
+  // output).
+  static constexpr int kFlushPer = kMaxK / kBlock;
+  static_assert(kFlushPer * kBlock == kMaxK, "the lanes' flush slots cover k");
   __device__ __forceinline__ bool flush(uint32_t from, uint32_t to) const {
     bool ok = true;
-    for (uint32_t j = from + threadIdx.x; j < to; j += kBlock) ok &= store(j, (int32_t)stage[j]);
+    int32_t e[kFlushPer], pg[kFlushPer];
+    bool v[kFlushPer];
+#pragma unroll
+    for (int u = 0; u < kFlushPer; ++u) {
+      const uint32_t j = from + threadIdx.x + (uint32_t)u * kBlock;
+      v[u] = j < to;
+      e[u] = v[u] ? (int32_t)stage[j] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kFlushPer; ++u)   // never index the table past the row
+      pg[u] = (v[u] && (uint32_t)e[u] < len) ? page(e[u]) : 0;
+#pragma unroll
+    for (int u = 0; u < kFlushPer; ++u)
+      if (v[u]) ok &= store_page(from + threadIdx.x + (uint32_t)u * kBlock, e[u], pg[u]);
     return ok;
   }
 };
