@@ -931,7 +931,9 @@ __device__ __forceinline__ void refine(const Src& src, const Refine& p, Smem& sh
 // lane-group so the threshold scan is bank-conflict free, lives in the (free)
 // LDS list region; emission and compaction offsets come from one block scan
 // of per-lane counts. Survivors continue in LDS as composite keys.
-template <int J>
+// CLEARED: the caller has already zeroed kWideWords words of the list (the
+// largest histogram this pass uses).
+template <int J, bool CLEARED = false>
 __device__ __forceinline__ void resolve_regs(const uint32_t (&kd)[J], const uint32_t (&ps)[J], uint32_t n,
                                              const Refine& p, Smem& sh, const RowOut& o) {
   static_assert(J * kBlock + 2 * kBlock <= kListCap, "per-lane sink slots lie past the candidates");
@@ -963,8 +965,10 @@ __device__ __forceinline__ void resolve_regs(const uint32_t (&kd)[J], const uint
   };
   uint32_t* hist = reinterpret_cast<uint32_t*>(sh.list);
   const uint32_t words = (mask + 1) + ((mask + 1) >> pad);
-  for (int i = t; i < (int)words; i += kBlock) hist[i] = 0;
-  __syncthreads();
+  if constexpr (!CLEARED) {
+    for (int i = t; i < (int)words; i += kBlock) hist[i] = 0;
+    __syncthreads();
+  }
   // Invalid slots add into this lane's own sink word past the histogram (one
   // shared sink would serialise whole waves on a single address).
   const uint32_t sink = words + (uint32_t)t;
@@ -1145,7 +1149,11 @@ __device__ __forceinline__ void resolve_global_regs(const GroupState* g, const u
     const uint32_t i = (uint32_t)j * kBlock + t;
     e[j] = i < n ? ld_agent(slab + i) : 0ull;
   }
-  if (t < 4) sh.range[t] = ld_agent(&g->range[t]);
+  const uint32_t rng = t < 4 ? ld_agent(&g->range[t]) : 0u;
+  // The first pass's histogram is cleared while the candidates arrive.
+  static_assert(kWideWords % 4 == 0, "cleared in 16-byte stores");
+  for (int i = t; i < kWideWords / 4; i += kBlock) reinterpret_cast<uint4*>(sh.list)[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (t < 4) sh.range[t] = rng;
   __syncthreads();
   const Refine p = make_refine(sh.range, need, n);
   uint32_t kd[J], ps[J];
@@ -1154,7 +1162,7 @@ __device__ __forceinline__ void resolve_global_regs(const GroupState* g, const u
     kd[j] = (uint32_t)(e[j] >> 32) - p.lo32;
     ps[j] = (uint32_t)e[j];
   }
-  resolve_regs<J>(kd, ps, n, p, sh, o);
+  resolve_regs<J, true>(kd, ps, n, p, sh, o);
 }
 
 // The last workgroup of a split row resolves its threshold bin from the
