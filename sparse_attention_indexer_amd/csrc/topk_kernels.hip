@@ -697,6 +697,50 @@ __device__ __forceinline__ void find_threshold_raw(const uint32_t* hist, uint32_
   __syncthreads();
 }
 
+// One scan of a chunk's histogram from the top (as find_threshold_raw) that
+// finds two thresholds at once, the bins holding the need1-th and need2-th
+// largest scores (*b1, *b2: left as preset when the chunk holds fewer), and
+// keeps each thread's exclusive prefix in cum[t] (lane t covers ordered bins
+// kBins - 1 - 2t and kBins - 2 - 2t), from which count_above() later reads
+// the count above any bin without another scan.
+__device__ __forceinline__ void two_thresholds_raw(const uint32_t* hist, uint32_t need1, uint32_t need2,
+                                                   uint32_t* scratch, uint32_t* cum, uint32_t* b1, uint32_t* b2) {
+  constexpr int PB = kBins / kBlock;
+  const int t = threadIdx.x;
+  uint32_t h[PB], s = 0;
+#pragma unroll
+  for (int j = 0; j < PB; ++j) {
+    const uint32_t b = (uint32_t)(kBins - 1 - (t * PB + j));
+    h[j] = (b >= kFirstBin && b <= kLastBin) ? hist[raw_of_bin(b)] : 0u;
+    s += h[j];
+  }
+  uint32_t c = block_exclusive_add(s, scratch);
+  cum[t] = c;
+#pragma unroll
+  for (int j = 0; j < PB; ++j) {
+    const uint32_t b = (uint32_t)(kBins - 1 - (t * PB + j));
+    if (c < need1 && need1 <= c + h[j]) *b1 = b;
+    if (c < need2 && need2 <= c + h[j]) *b2 = b;
+    c += h[j];
+  }
+  __syncthreads();
+}
+
+// Scores of the chunk in bins above ordered bin b, from two_thresholds_raw's
+// prefixes (uniform: every lane reads the same words).
+__device__ __forceinline__ uint32_t count_above(const uint32_t* hist, const uint32_t* cum, uint32_t b) {
+  constexpr int PB = kBins / kBlock;
+  static_assert(PB == 2, "two bins per lane");
+  const uint32_t from_top = (uint32_t)(kBins - 1) - b;
+  const uint32_t tb = from_top / PB;
+  uint32_t above = cum[tb];
+  if (from_top % PB) {
+    const uint32_t b0 = (uint32_t)(kBins - 1) - tb * PB;
+    above += (b0 >= kFirstBin && b0 <= kLastBin) ? hist[raw_of_bin(b0)] : 0u;
+  }
+  return uni(above);
+}
+
 // Compressed composite key of a boundary candidate: the FP32 key offset from
 // the smallest candidate key, then the position reversed so that lower
 // positions rank higher. Distinct for distinct positions, so the top `need`
@@ -1221,13 +1265,15 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
   const uint32_t k = (uint32_t)a.k;
   GroupState* g = a.groups + w.group;
 
-  // Only bins at or above this chunk's own k-th bin can hold the row's k-th.
-  uint32_t bloc = 0;
-  if ((uint32_t)(end - begin) >= k) {
-    if (t == 0) sh.res[0] = 0;
-    find_threshold_raw(sh.lhist, k, sh.scratch, sh.res);
-    bloc = uni(sh.res[0]);
-  }
+  // Only bins at or above this chunk's own k-th bin can hold the row's k-th
+  // (bloc). One scan also finds the bin of its T-th largest score (bpre, for
+  // the pre-read below) and keeps the prefixes that later give the count
+  // above the row's threshold bin. Both stay 0 when the chunk is shorter.
+  const uint32_t T = resident ? min(k, 2u * ((k + G - 1u) / G) + 64u) : k;
+  uint32_t* cum = sh.outpos;   // free until the extraction stages outputs
+  if (t == 0) sh.res[0] = sh.res[3] = 0;
+  two_thresholds_raw(sh.lhist, k, T, sh.scratch, cum, &sh.res[0], &sh.res[3]);
+  const uint32_t bloc = uni(sh.res[0]);
   // The scores of the chunk that no merged bin counts go to g->arrive, so the
   // merged bins and that count add up to the row length once every
   // workgroup's atomics have landed: there is no separate arrival (and no
@@ -1241,30 +1287,31 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
       merged += h;
     }
   }
-  {
-    uint32_t tot_merged;
-    block_exclusive_add(merged, sh.scratch, &tot_merged);
-    if (t == 0) {
-      const uint32_t chunk = end > begin ? (uint32_t)(end - begin) : 0u;
-      __hip_atomic_fetch_add(&g->arrive, chunk - tot_merged, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+  const uint32_t chunk = end > begin ? (uint32_t)(end - begin) : 0u;
   // While the other workgroups merge: list the positions at or above the
-  // local k-th bin and start reading their scores and block-table entries.
+  // local T-th bin and start reading their scores and block-table entries.
   uint32_t* pre = reinterpret_cast<uint32_t*>(sh.list + kStageCap);
   float pv[kPreRegs];
   int32_t ppg[kPreRegs];
   uint32_t n_pre = 0xFFFFFFFFu, bpre = kNotFound;
-  if (resident) {
-    const uint32_t T = min(k, 2u * ((k + G - 1u) / G) + 64u);
-    if (t == 0) sh.res[0] = 0;
-    if ((uint32_t)(end - begin) >= T) find_threshold_raw(sh.lhist, T, sh.scratch, sh.res);
-    else __syncthreads();
-    bpre = uni(sh.res[0]);
+  if (!resident) {
+    uint32_t tot_merged;
+    block_exclusive_add(merged, sh.scratch, &tot_merged);
+    if (t == 0)
+      __hip_atomic_fetch_add(&g->arrive, chunk - tot_merged, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    bpre = uni(sh.res[3]);
     const uint64_t pm = interest_mask(hk, cut_of_bin(bpre).vlo);
+    // One scan for both the merged count (high half) and the listing offsets
+    // (low half): a resident chunk holds at most 32,768 scores, so neither
+    // total reaches 2^16.
+    static_assert(kTile < (1 << 16), "merged and listed counts share one scan");
     uint32_t tot;
-    uint32_t off = block_exclusive_add((uint32_t)__popcll(pm), sh.scratch, &tot);
-    n_pre = uni(tot);
+    uint32_t off = block_exclusive_add((merged << 16) | (uint32_t)__popcll(pm), sh.scratch, &tot);
+    off &= 0xFFFFu;
+    n_pre = uni(tot) & 0xFFFFu;
+    if (t == 0)
+      __hip_atomic_fetch_add(&g->arrive, chunk - (uni(tot) >> 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (n_pre <= (uint32_t)kPreCap) {
       uint64_t m = pm;
       while (m) {
@@ -1323,14 +1370,7 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
   const uint32_t bstar = found ? r0 : kLastBin;
   const uint32_t n_above = found ? uni(sh.res[1]) : 0u, cnt = found ? uni(sh.res[2]) : 0u;
   const Cut cut = cut_of_bin(bstar);
-  uint32_t la = 0;
-  for (int r = t; r < kBins; r += kBlock) {
-    const uint32_t b = bin_of_raw((uint32_t)r);
-    la += (found && b > bstar && b <= kLastBin) ? sh.lhist[r] : 0u;
-  }
-  uint32_t local_above;
-  block_exclusive_add(la, sh.scratch, &local_above);
-  local_above = uni(local_above);
+  const uint32_t local_above = found ? count_above(sh.lhist, cum, bstar) : 0u;
   const uint32_t local_cnt = found ? uni(sh.lhist[raw_of_bin(bstar)]) : 0u;
   const bool keep = found && (int64_t)cnt <= a.cand_cap;
   const bool stage = keep && local_cnt <= (uint32_t)kStageCap;   // candidates staged in LDS
