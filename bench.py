@@ -172,6 +172,41 @@ def calibrate_copy(mib: int, reps: int = 3) -> None:
     say(f"[bench] copy calibration: {reps} x {mib} MiB device-to-device")
 
 
+def read_ceiling(headline_bytes: int, reps: int = 20) -> dict:
+    """The box's streaming-read ceiling for the selection kernel's load pattern
+    (topk_debug_stream_read): the headline's byte count from cold rotated
+    copies (>= 512 MB, so none is cache-resident), and one 2 GiB buffer for
+    the large-transfer rate. Each launch is timed with HIP events that record
+    the kernel's own start and end (as the selection kernel's timing is)."""
+    import torch
+    from sparse_attention_indexer_amd import topk
+    dev = torch.device("cuda:0")
+    out = None
+    res = {"kernel": "topk_stream_read_kernel (16-byte loads, 256 x 512 lanes, 16 vectors in flight per lane)",
+           "timing": "kernel events (the dispatch's own start and end), p50 of %d" % reps}
+    for label, nbytes in (("headline_bytes", headline_bytes), ("2gib", 2 << 30)):
+        n = nbytes // 16 * 4
+        copies = max(1, math.ceil((512 << 20) / (n * 4)))
+        bufs = [torch.rand(n, dtype=torch.float32, device=dev) for _ in range(copies)]
+        out = topk.topk_debug_stream_read(bufs[0], out)
+        torch.cuda.synchronize()
+        times = []
+        for i in range(reps + 3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            topk.topk_debug_stream_read(bufs[i % copies], out, events=(a, b))
+            b.synchronize()
+            if i >= 3:
+                times.append(a.elapsed_time(b) * 1e3)
+        us = statistics.median(times)
+        res[label] = {"bytes": n * 4, "us_p50": round(us, 3), "GB/s": round(n * 4 / us / 1e3, 1),
+                      "copies": copies}
+        del bufs
+        torch.cuda.empty_cache()
+    say(f"[bench] read ceiling: {res['headline_bytes']['GB/s']} GB/s at {headline_bytes} B, "
+        f"{res['2gib']['GB/s']} GB/s at 2 GiB")
+    return res
+
+
 def cpu_baseline(w, seconds: float):
     """The oracle as it stands, over whole batches, until `seconds` have passed."""
     import oracle
@@ -259,6 +294,8 @@ def main() -> int:
     ap.add_argument("--warm-cache", action="store_true", help="reuse one input copy (cache-resident)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="after timing, copy this many MiB device-to-device (counter calibration)")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the streaming-read ceiling measurement")
     ap.add_argument("--sweep", default="",
                     help="comma list from {c1..c5, cp8_7x125k}: one JSON line per workload")
     args = ap.parse_args()
@@ -283,6 +320,7 @@ def main() -> int:
         results[n] = (w, measure(w, args.steps, args.warmup, rotate=not args.warm_cache))
     if args.calibrate_copy_mb:
         calibrate_copy(args.calibrate_copy_mb)
+    ceiling = None if args.no_read_ceiling else read_ceiling(int(results[names[0]][0].lengths.sum()) * 4)
 
     head = names[0]
     w, res = results[head]
@@ -334,6 +372,7 @@ def main() -> int:
             "kernel_us": round(res["select_ms"] * 1e3, 3),
         },
         "cpu_baseline": base,
+        "hbm_read_ceiling": ceiling,
         "select_us": {"mean": round(res["select_ms"] * 1e3, 3), "p10": round(res["select_p10_ms"] * 1e3, 3),
                       "p50": round(res["select_p50_ms"] * 1e3, 3), "p90": round(res["select_p90_ms"] * 1e3, 3),
                       "stream_events_mean": round(res["select_stream_ms"] * 1e3, 3)},

@@ -185,6 +185,22 @@ int64_t topk_register_capacity(void);
  */
 topk_status topk_debug_keys(const float* x, int64_t n, uint32_t* bin_out, uint32_t* key32_out, void* stream);
 
+/*
+ * Measurement hook: the device's streaming-read ceiling for this access
+ * pattern. Reads the whole 16-byte vectors of x[0, n) (device, n >= 0,
+ * 16-byte aligned) once with the selection kernel's loads (512-lane
+ * workgroups, one per compute unit, each lane keeping 16 vectors in flight)
+ * and writes one partial sum per workgroup to out[0, topk_stream_read_groups())
+ * (device), so the reads cannot be elided. Enqueued on `stream`. When both
+ * start_event and stop_event (hipEvent_t) are given, they record the
+ * kernel's own start and end, as in topk_select_paged_timed; else pass NULL.
+ * Status: OK, INVALID_ARG (NULL pointer with n > 0, misaligned x, n < 0,
+ * only one event), HIP.
+ */
+topk_status topk_debug_stream_read(const float* x, int64_t n, float* out, void* stream, void* start_event,
+                                   void* stop_event);
+int32_t topk_stream_read_groups(void);
+
 const char* topk_status_string(topk_status s);
 
 #ifdef __cplusplus

@@ -19,6 +19,9 @@ hipError_t launch_select(const SelectArgs& a, int grid, bool vec, bool stream_it
 hipError_t launch_fill(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_debug_keys(const float* x, int64_t n, uint32_t* bin, uint32_t* k32, hipStream_t s);
 hipError_t select_occupancy(int* per_cu);
+hipError_t launch_stream_read(const float* x, int64_t n, float* out, hipStream_t s, hipEvent_t start,
+                              hipEvent_t stop);
+int stream_read_groups();
 }  // namespace satopk
 
 using namespace satopk;
@@ -297,6 +300,19 @@ topk_status topk_debug_keys(const float* x, int64_t n, uint32_t* bin_out, uint32
              ? TOPK_OK
              : TOPK_ERR_HIP;
 }
+
+topk_status topk_debug_stream_read(const float* x, int64_t n, float* out, void* stream, void* start_event,
+                                   void* stop_event) {
+  if (n < 0 || (n > 0 && (!x || !out)) || ((uintptr_t)x % 16) != 0) return TOPK_ERR_INVALID_ARG;
+  if (!start_event != !stop_event) return TOPK_ERR_INVALID_ARG;
+  if (n / 4 == 0) return TOPK_OK;   // (a tail of fewer than 4 floats is not read)
+  return launch_stream_read(x, n, out, (hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event) ==
+                 hipSuccess
+             ? TOPK_OK
+             : TOPK_ERR_HIP;
+}
+
+int32_t topk_stream_read_groups(void) { return stream_read_groups(); }
 
 const char* topk_status_string(topk_status s) {
   switch (s) {

@@ -1804,6 +1804,38 @@ __global__ void topk_debug_keys_kernel(const float* x, int64_t n, uint32_t* bin,
   }
 }
 
+// Streaming-read ceiling: each workgroup reads its contiguous share of x with
+// the selection kernel's load pattern (lane t takes vector q * kBlock + t,
+// 16 vectors in flight) and writes one partial sum.
+constexpr int kStreamReadGroups = 256;
+__global__ void __launch_bounds__(kBlock) topk_stream_read_kernel(const float4* x, int64_t nvec, int64_t per_group,
+                                                                  float* out) {
+  __shared__ float part[kWaves];
+  const int64_t begin = (int64_t)blockIdx.x * per_group;
+  const int64_t end = min(begin + per_group, nvec);
+  float acc = 0.f;
+  for (int64_t base = begin; base < end; base += (int64_t)kEpt / 4 * kBlock) {
+    float4 v[kEpt / 4];
+#pragma unroll
+    for (int q = 0; q < kEpt / 4; ++q) {
+      const int64_t i = base + (int64_t)q * kBlock + threadIdx.x;
+      v[q] = i < end ? x[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int q = 0; q < kEpt / 4; ++q) acc += (v[q].x + v[q].y) + (v[q].z + v[q].w);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if (lane() == 0) part[threadIdx.x / 64] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) sum += part[w];
+    out[blockIdx.x] = sum;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Host-side launchers (called by the C ABI in topk_api.hip).
 // ---------------------------------------------------------------------------
@@ -1855,6 +1887,22 @@ hipError_t launch_debug_keys(const float* x, int64_t n, uint32_t* bin, uint32_t*
   hipLaunchKernelGGL(topk_debug_keys_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, n, bin, k32);
   return hipGetLastError();
 }
+
+hipError_t launch_stream_read(const float* x, int64_t n, float* out, hipStream_t s, hipEvent_t start,
+                              hipEvent_t stop) {
+  const int64_t nvec = n / 4;
+  const int64_t per_group = (nvec + kStreamReadGroups - 1) / kStreamReadGroups;
+  const float4* xv = reinterpret_cast<const float4*>(x);
+  if (start && stop)
+    hipExtLaunchKernelGGL(topk_stream_read_kernel, dim3(kStreamReadGroups), dim3(kBlock), 0, s, start, stop, 0, xv,
+                          nvec, per_group, out);
+  else
+    hipLaunchKernelGGL(topk_stream_read_kernel, dim3(kStreamReadGroups), dim3(kBlock), 0, s, xv, nvec, per_group,
+                       out);
+  return hipGetLastError();
+}
+
+int stream_read_groups() { return kStreamReadGroups; }
 
 hipError_t select_occupancy(int* per_cu) {
   int a = 0, b = 0;

@@ -63,6 +63,7 @@ def load_library():
         "topk_select_paged_timed": [P, V, V, I64, V, I32, V, I64, I32, V, V, I64, V, S, V, V, V],
         "topk_read_status": [V, S, ctypes.POINTER(I32), V],
         "topk_debug_keys": [V, I64, V, V, V],
+        "topk_debug_stream_read": [V, I64, V, V, V, V],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
@@ -70,6 +71,8 @@ def load_library():
         f.restype = ctypes.c_int
     lib.topk_register_capacity.argtypes = []
     lib.topk_register_capacity.restype = ctypes.c_int64
+    lib.topk_stream_read_groups.argtypes = []
+    lib.topk_stream_read_groups.restype = ctypes.c_int32
     lib.topk_status_string.argtypes = [ctypes.c_int]
     lib.topk_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -199,6 +202,22 @@ def topk_debug_keys(x: torch.Tensor, stream=None) -> tuple[torch.Tensor, torch.T
     _check("topk_debug_keys", load_library().topk_debug_keys(x.data_ptr(), x.numel(), bins.data_ptr(),
                                                              keys.data_ptr(), _stream(stream)))
     return bins, keys
+
+
+def topk_debug_stream_read(x: torch.Tensor, out: torch.Tensor | None = None, stream=None,
+                           events=None) -> torch.Tensor:
+    """One streaming read of ``x`` (float32, contiguous, 16-byte aligned) with
+    the selection kernel's load pattern; returns the per-workgroup partial sums.
+    ``events``: optional (start, stop) torch.cuda.Event pair that records the
+    kernel's own start and end."""
+    _need(x, torch.float32, "x")
+    lib = load_library()
+    if out is None:
+        out = torch.empty(int(lib.topk_stream_read_groups()), dtype=torch.float32, device=x.device)
+    ev = (None, None) if events is None else (_event_handle(events[0]), _event_handle(events[1]))
+    _check("topk_debug_stream_read", lib.topk_debug_stream_read(x.data_ptr(), x.numel(), out.data_ptr(),
+                                                                _stream(stream), ev[0], ev[1]))
+    return out
 
 
 # --- convenience wrapper ----------------------------------------------------------

@@ -29,6 +29,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("topk_query_sizes", "topk_plan", "topk_select_paged", "topk_workspace_init",
               "topk_read_status", "topk_status_string", "topk_register_capacity", "topk_debug_keys",
+              "topk_debug_stream_read", "topk_stream_read_groups",
               "topk_select_paged_timed"):
         assert n in names
 
@@ -88,6 +89,9 @@ def test_null_arguments_rejected(T):
     v = ctypes.c_int32(0)
     assert lib.topk_read_status(None, 256, ctypes.byref(v), None) == T.TOPK_ERR_INVALID_ARG
     assert lib.topk_debug_keys(None, 5, None, None, None) == T.TOPK_ERR_INVALID_ARG
+    assert lib.topk_debug_stream_read(None, 8, None, None, None, None) == T.TOPK_ERR_INVALID_ARG
+    assert lib.topk_debug_stream_read(None, -1, None, None, None, None) == T.TOPK_ERR_INVALID_ARG
+    assert lib.topk_stream_read_groups() >= 1
     bad = T.make_config(0, 7, 80_000)
     assert lib.topk_plan(ctypes.byref(bad), None, 7, None, 0, None) == T.TOPK_ERR_INVALID_ARG
     assert lib.topk_select_paged(ctypes.byref(bad), None, None, 0, None, 7, None, 0, 64,

@@ -274,3 +274,18 @@ def test_guessed_tile_paths(max_len, exact, alphabet):
     _gpu.say(f"[guess] 9 rows, max_len {max_len}, exact {exact}, alphabet {alphabet}")
     for got in _gpu.run_gpu(w, "auto", repeat=2):
         _gpu.assert_matches_oracle(w, got, f"guessed tile {max_len}")
+
+
+@pytest.mark.parametrize("n", [0, 3, 4, 1_000_003, 7_000_000])
+def test_stream_read_hook_reads_every_vector(n):
+    """The read-ceiling hook reads each 16-byte vector of x exactly once: its
+    partial sums add up to the sum of x's whole vectors (a tail of fewer than
+    4 floats is not read)."""
+    from sparse_attention_indexer_amd import topk
+    g = torch.Generator(device="cuda:0").manual_seed(n)
+    x = torch.rand(max(n, 1), generator=g, device="cuda:0")[:n]
+    out = torch.zeros(256, dtype=torch.float32, device="cuda:0")
+    topk.topk_debug_stream_read(x, out)
+    torch.cuda.synchronize()
+    want = x[: n // 4 * 4].double().sum().item()
+    assert abs(out.double().sum().item() - want) <= 1e-4 * max(1.0, want)
