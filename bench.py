@@ -35,7 +35,7 @@ ROTATION_BYTES = 512 << 20
 IN_KERNEL_PLAN_ROWS = 512      # batches this small are planned inside topk_select_paged
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "topk_select_kernel_7x1m_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "sparse_attention_indexer_amd", "csrc", f)
-                  for f in ("topk_kernels.hip", "topk_device.hpp", "topk_layout.hpp")]
+                  for f in ("topk_kernels.hip", "topk_device.hpp", "topk_layout.hpp", "topk_plan.hpp")]
 
 DESCRIPTIONS = {
     "7x1m": "7x1M k=2048: 7 rows x 1,000,000 FP32 scores ~N(0,1), 1% in [3.0,3.0005), "
