@@ -289,3 +289,44 @@ def test_stream_read_hook_reads_every_vector(n):
     torch.cuda.synchronize()
     want = x[: n // 4 * 4].double().sum().item()
     assert abs(out.double().sum().item() - want) <= 1e-4 * max(1.0, want)
+
+
+@pytest.mark.parametrize("rows,max_len", [(7, 80_000), (600, 6_000)], ids=["7x80k-in-kernel-plan", "600-rows-plan-kernel"])
+def test_plan_and_select_replay_from_a_hip_graph(rows, max_len):
+    """topk_plan + topk_select_paged captured once into a HIP graph and
+    replayed four times, with new scores and lengths copied in eagerly (and a
+    synchronisation) before each replay; every replay must match the oracle
+    for its own inputs. 600 rows take the planning kernel, 7 rows plan inside
+    the selection kernel (the split rows' per-row state must be left reset
+    after each replay)."""
+    from sparse_attention_indexer_amd import topk
+    dev = torch.device("cuda:0")
+    cases = [synth.random_case(900 + rows + i, rows, max_len, k=2048, exact_len=(i % 2 == 0)) for i in range(2)]
+    tk = topk.TopK(2048, rows, max_len, device=dev)
+    sc = torch.from_numpy(np.ascontiguousarray(cases[0].scores)).to(dev)
+    ln = torch.from_numpy(cases[0].lengths).to(dev)
+    bt = torch.from_numpy(np.ascontiguousarray(cases[0].block_table)).to(dev)
+    slots = torch.empty((rows, 2048), dtype=torch.int32, device=dev)
+    idx = torch.empty_like(slots)
+    assert cases[0].bt_row_stride == cases[1].bt_row_stride and cases[0].block_table.shape == cases[1].block_table.shape
+    # eager warm-up on the capture's buffers, then the capture
+    tk.plan(ln)
+    tk.select(sc, ln, bt, cases[0].bt_row_stride, cases[0].page_size, out_slots=slots, out_indices=idx)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        tk.plan(ln)
+        tk.select(sc, ln, bt, cases[0].bt_row_stride, cases[0].page_size, out_slots=slots, out_indices=idx)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        w = cases[rep % 2]
+        sc.copy_(torch.from_numpy(np.ascontiguousarray(w.scores)))
+        ln.copy_(torch.from_numpy(w.lengths))
+        bt.copy_(torch.from_numpy(np.ascontiguousarray(w.block_table)))
+        slots.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _gpu.say(f"[graph] rows {rows} replay {rep}")
+        _gpu.assert_matches_oracle(w, (idx.cpu().numpy(), slots.cpu().numpy()), f"graph replay {rep}")
+    assert tk.status() == 0
