@@ -14,7 +14,7 @@ static_assert(satopk::kInKernelPlanRows <= satopk::kBlock, "one row per thread")
 
 namespace satopk {
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
-hipError_t launch_select(const SelectArgs& a, int grid, bool vec, bool stream_items, bool overlap, hipStream_t s,
+hipError_t launch_select(const SelectArgs& a, int grid, bool vec, bool stream_items, int overlap, hipStream_t s,
                          hipEvent_t start, hipEvent_t stop);
 hipError_t launch_fill(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_debug_keys(const float* x, int64_t n, uint32_t* bin, uint32_t* k32, hipStream_t s);
@@ -247,9 +247,10 @@ topk_status select_impl(const topk_config* cfg, const void* plan, const float* s
   }
   const bool vec = ((uintptr_t)scores % 16 == 0) && (score_row_stride % 4 == 0);
   // The planning overlaps the guessed tile's loads when that tile is at least
-  // half a tile long.
+  // half a tile long (all 16 vector groups) or at most 8,192 scores (the
+  // first 4).
   const int64_t guess_len = a.guess_groups > 1 ? a.guess_chunk : cfg->max_len;
-  const bool overlap = here && guess_len >= kTile / 2 && guess_len <= kTile;
+  const int overlap = !here ? 0 : (guess_len >= kTile / 2 && guess_len <= kTile) ? 16 : (guess_len <= 4 * kBlock * 4) ? 4 : 0;
   return launch_select(a, s.grid, vec, items_may_stream(cfg, s), overlap, (hipStream_t)stream, (hipEvent_t)start_event,
                        (hipEvent_t)stop_event) ==
                  hipSuccess

@@ -414,14 +414,18 @@ __device__ __forceinline__ void load_raw(const float* rowp, int32_t base, int32_
 // that overlaps it.) Consumers mask positions past `end` as for load_raw.
 constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
 
-template <bool VEC>
+// Only the first NV vector groups are read; the others hold zeros (the
+// caller guarantees [base, end) lies within them).
+template <bool VEC, int NV = kEpt / 4>
 __device__ __forceinline__ void load_raw_buffer(const float* rowp, int32_t base, int32_t end,
                                                 float4 (&x)[kEpt / 4]) {
   const int32_t n = end > base ? min(end - base, (int32_t)kTile) : 0;
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(rowp) + base, (short)0, n * 4, kBufferFlags);
 #pragma unroll
-  for (int q = 0; q < kEpt / 4; ++q) {
+  for (int q = NV; q < kEpt / 4; ++q) x[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int q = 0; q < NV; ++q) {
     const int32_t off = (q * kBlock + (int)threadIdx.x) * 16;   // bytes from `base`
     if constexpr (VEC) {
       x[q] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
@@ -1678,14 +1682,15 @@ __device__ __forceinline__ int plan_here(const SelectArgs& a, Smem& sh, int32_t 
 // lengths arrive, then plans; the loads are used when the real plan gives the
 // same chunk (every batch of equal lengths), and the tile is then packed,
 // binned and parked in LDS. Returns whether it was; num_items as plan_here.
-// OVERLAP: the lengths are requested first and the tile goes through a
+// OVERLAP > 0: the lengths are requested first and the tile (its first
+// OVERLAP vector groups, which hold the guessed chunk) goes through a
 // buffer resource (no per-lane branches), so the planning waits for the
 // lengths only and runs while the tile arrives. Without it, the tile is
 // converted as it arrives and the planning follows.
-template <bool VEC, bool OVERLAP>
+template <bool VEC, int OVERLAP>
 __device__ __forceinline__ bool guess_and_plan(const SelectArgs& a, Smem& sh, int& num_items) {
   int32_t len_t = 0;
-  if constexpr (OVERLAP) {
+  if constexpr (OVERLAP > 0) {
     // (loads complete in order: waiting for the length does not wait for the tile)
     len_t = (int)threadIdx.x < a.num_rows ? a.lengths[threadIdx.x] : 0;
     asm volatile("" ::: "memory");
@@ -1707,12 +1712,12 @@ __device__ __forceinline__ bool guess_and_plan(const SelectArgs& a, Smem& sh, in
       srow = B;
       send = L;
     }
-    if constexpr (OVERLAP) {
-      if (srow < 0 || send - sbeg > kTile) {   // no guess: nothing is read
+    if constexpr (OVERLAP > 0) {
+      if (srow < 0 || send - sbeg > OVERLAP * kBlock * 4) {   // no guess that fits: nothing is read
         srow = -1;
         sbeg = send = 0;
       }
-      load_raw_buffer<VEC>(a.scores + (int64_t)max(srow, 0) * a.stride, sbeg, send, x);
+      load_raw_buffer<VEC, OVERLAP>(a.scores + (int64_t)max(srow, 0) * a.stride, sbeg, send, x);
     } else {
       if (srow >= 0 && send - sbeg <= kTile) load_raw<VEC>(a.scores + (int64_t)srow * a.stride, sbeg, send, x);
       else srow = -1;
@@ -1720,14 +1725,14 @@ __device__ __forceinline__ bool guess_and_plan(const SelectArgs& a, Smem& sh, in
   }
   // (the barriers of the planning order this clear before any histogram add)
   if (srow >= 0) hist_copies_clear(reinterpret_cast<uint32_t*>(sh.list));
-  if constexpr (!OVERLAP) len_t = (int)threadIdx.x < a.num_rows ? a.lengths[threadIdx.x] : 0;
+  if constexpr (OVERLAP == 0) len_t = (int)threadIdx.x < a.num_rows ? a.lengths[threadIdx.x] : 0;
   num_items = plan_here(a, sh, len_t);
-  if constexpr (OVERLAP) {
+  if constexpr (OVERLAP > 0) {
     // Keep the tile's first use here: the compiler would otherwise convert
     // each vector as it arrives, ahead of the planning, and the planning
     // would then wait for the whole tile.
 #pragma unroll
-    for (int q = 0; q < kEpt / 4; ++q) asm volatile("" : "+v"(x[q].x), "+v"(x[q].y), "+v"(x[q].z), "+v"(x[q].w));
+    for (int q = 0; q < OVERLAP; ++q) asm volatile("" : "+v"(x[q].x), "+v"(x[q].y), "+v"(x[q].z), "+v"(x[q].w));
   }
   if (num_items < 0) return false;
   // Park the tile if the real plan gave the guessed chunk (the same row and
@@ -1749,11 +1754,12 @@ __device__ __forceinline__ bool guess_and_plan(const SelectArgs& a, Smem& sh, in
   return parked;
 }
 
-// OVERLAP: the in-kernel planning overlaps the guessed tile's loads (chosen
-// by the host for guessed tiles of at least half a tile; smaller ones arrive
-// about as soon as the lengths do, and skipping their empty vector groups
-// is worth more than the overlap).
-template <bool VEC, bool STREAM, bool OVERLAP>
+// OVERLAP > 0: the in-kernel planning overlaps the loads of the guessed
+// tile's first OVERLAP vector groups (chosen by the host: 16 for guessed
+// tiles of at least half a tile, 4 for those of at most 8,192 scores; in
+// between, the conditional loads skip empty vector groups, which is worth
+// more than the overlap).
+template <bool VEC, bool STREAM, int OVERLAP>
 __global__ void __launch_bounds__(kBlock) topk_select_kernel(SelectArgs a) {
   __shared__ Smem sh;
   int num_items;
@@ -1846,7 +1852,7 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
 
 // With events, they record the dispatch's own start and end (the same
 // interval a kernel trace reports), not the stream position around it.
-template <bool VEC, bool STREAM, bool OVERLAP>
+template <bool VEC, bool STREAM, int OVERLAP>
 void launch_select_t(const SelectArgs& a, int grid, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   void (*kernel)(SelectArgs) = topk_select_kernel<VEC, STREAM, OVERLAP>;
   if (start || stop)
@@ -1855,18 +1861,20 @@ void launch_select_t(const SelectArgs& a, int grid, hipStream_t s, hipEvent_t st
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), 0, s, a);
 }
 
-hipError_t launch_select(const SelectArgs& a, int grid, bool vec, bool stream_items, bool overlap, hipStream_t s,
+hipError_t launch_select(const SelectArgs& a, int grid, bool vec, bool stream_items, int overlap, hipStream_t s,
                          hipEvent_t start, hipEvent_t stop) {
   if (vec && stream_items) {
-    if (overlap) launch_select_t<true, true, true>(a, grid, s, start, stop);
-    else launch_select_t<true, true, false>(a, grid, s, start, stop);
+    if (overlap == 16) launch_select_t<true, true, 16>(a, grid, s, start, stop);
+    else if (overlap == 4) launch_select_t<true, true, 4>(a, grid, s, start, stop);
+    else launch_select_t<true, true, 0>(a, grid, s, start, stop);
   } else if (vec) {
-    if (overlap) launch_select_t<true, false, true>(a, grid, s, start, stop);
-    else launch_select_t<true, false, false>(a, grid, s, start, stop);
+    if (overlap == 16) launch_select_t<true, false, 16>(a, grid, s, start, stop);
+    else if (overlap == 4) launch_select_t<true, false, 4>(a, grid, s, start, stop);
+    else launch_select_t<true, false, 0>(a, grid, s, start, stop);
   } else if (stream_items) {
-    launch_select_t<false, true, false>(a, grid, s, start, stop);
+    launch_select_t<false, true, 0>(a, grid, s, start, stop);
   } else {
-    launch_select_t<false, false, false>(a, grid, s, start, stop);
+    launch_select_t<false, false, 0>(a, grid, s, start, stop);
   }
   return hipGetLastError();
 }
@@ -1906,12 +1914,14 @@ int stream_read_groups() { return kStreamReadGroups; }
 
 hipError_t select_occupancy(int* per_cu) {
   int a = 0, b = 0;
-  const void* kernels[6] = {(const void*)topk_select_kernel<true, true, false>,
-                            (const void*)topk_select_kernel<true, false, false>,
-                            (const void*)topk_select_kernel<true, true, true>,
-                            (const void*)topk_select_kernel<true, false, true>,
-                            (const void*)topk_select_kernel<false, true, false>,
-                            (const void*)topk_select_kernel<false, false, false>};
+  const void* kernels[8] = {(const void*)topk_select_kernel<true, true, 0>,
+                            (const void*)topk_select_kernel<true, false, 0>,
+                            (const void*)topk_select_kernel<true, true, 16>,
+                            (const void*)topk_select_kernel<true, false, 16>,
+                            (const void*)topk_select_kernel<true, true, 4>,
+                            (const void*)topk_select_kernel<true, false, 4>,
+                            (const void*)topk_select_kernel<false, true, 0>,
+                            (const void*)topk_select_kernel<false, false, 0>};
   int best = 1 << 30;
   for (const void* f : kernels) {
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, f, kBlock, 0);
