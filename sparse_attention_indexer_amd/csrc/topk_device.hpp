@@ -40,6 +40,14 @@ __device__ __forceinline__ uint32_t first_lane(uint64_t m) {
   return (uint32_t)__builtin_ctzll(m);
 }
 
+// Zero in a vector register, produced by an instruction the compiler cannot
+// see through: an address offset by it is divergent to the compiler.
+__device__ __forceinline__ uint32_t opaque_zero() {
+  uint32_t z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
+
 // A value every lane holds equally (an LDS broadcast), moved to a scalar
 // register so that it costs no VGPR and branches on it stay uniform.
 __device__ __forceinline__ uint32_t uni(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }

@@ -1389,8 +1389,12 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
     sh.cur_out = 0;
     sh.cur_list = 0;
     sh.range[0] = sh.range[1] = sh.range[2] = sh.range[3] = 0;
-    if (local_above) base_out = __hip_atomic_fetch_add(&g->emit, local_above, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (keep && local_cnt) base_cand = __hip_atomic_fetch_add(&g->cand, local_cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // The zero offset hides that one lane runs this: offered a uniform
+    // address, the compiler turns each fetch-add into its wave-aggregated
+    // form, which reads the result back at once and so waits here.
+    const uint32_t z = opaque_zero();
+    if (local_above) base_out = __hip_atomic_fetch_add(&g->emit + z, local_above, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (keep && local_cnt) base_cand = __hip_atomic_fetch_add(&g->cand + z, local_cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (keep && !stage) {
