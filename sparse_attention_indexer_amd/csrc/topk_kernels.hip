@@ -475,11 +475,16 @@ static_assert(kBins * kHistCopies * 4 <= kListCap * 8, "histogram copies fit in 
 // Pack a tile (as pack_tile) and bin it into the copies in one pass over the
 // vectors, in load order, so the atomics of vector q go out while later
 // vectors are still arriving.
+template <int NQ = kEpt / 4>
 __device__ __forceinline__ void pack_hist(const float4 (&x)[kEpt / 4], int32_t base, int32_t end,
                                           uint32_t (&hk)[kHk], uint32_t* hc) {
   const uint32_t c = threadIdx.x & (kHistCopies - 1);
+  // NQ < kEpt / 4: the caller guarantees end <= base + NQ * kBlock * 4, so
+  // the later vector groups hold no position below `end` (NaN throughout).
 #pragma unroll
-  for (int q = 0; q < kEpt / 4; ++q) {
+  for (int q = NQ; q < kEpt / 4; ++q) hk[2 * q] = hk[2 * q + 1] = kHalfNaN2;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
     const int32_t e = tile_pos(base, q, 0);
     uint32_t p0 = to_half2(x[q].x, x[q].y), p1 = to_half2(x[q].z, x[q].w);
     if (e + 4 > end) {  // tail vector: positions >= end become NaN
@@ -1615,32 +1620,51 @@ __device__ __forceinline__ PlanArgs plan_args_of(const SelectArgs& a) {
 __device__ __forceinline__ int plan_here(const SelectArgs& a, Smem& sh, int32_t len) {
   const int t = threadIdx.x;
   const int R = a.num_rows;
-  const bool longer = t < R && len > split_floor(plan_args_of(a));
-  uint64_t mine = longer ? (uint64_t)len + (1ull << 40) : 0ull;   // lengths < 2^31, rows < 2^23
-  mine = wave_sum_u64(mine);
-  const uint32_t tl = wave_sum_u32(longer ? (uint32_t)tiles_of(len) : 0u);
-  if (lane() == 0) {
-    sh.pl_red[t >> 6] = mine;
-    sh.pl_red2[t >> 6] = tl;
-  }
-  __syncthreads();
-  uint64_t packed = 0;
-  uint32_t tiles = 0;
+  // narrow (uniform): at most one wave of rows, and `len` is then row
+  // lane()'s length in every wave, so each wave reduces and scans on its own
+  // (cross-lane moves, no LDS exchange, no barrier). Otherwise `len` is row
+  // t's and the waves combine through LDS.
+  const bool narrow = R <= kWave;
+  const int r = t & (narrow ? kWave - 1 : kBlock - 1);
+  const bool longer = r < R && len > split_floor(plan_args_of(a));
+  // Wave sums (lengths < 2^31: 64 halves of 16 and 15 bits fit a word).
+  const uint32_t lo = wave_sum_u32(longer ? (uint32_t)len & 0xFFFFu : 0u);
+  const uint32_t hi = wave_sum_u32(longer ? (uint32_t)len >> 16 : 0u);
+  uint64_t total = ((uint64_t)hi << 16) + lo;
+  int32_t n_long = (int32_t)__popcll(__ballot(longer));
+  uint32_t tiles = wave_sum_u32(longer ? (uint32_t)tiles_of(len) : 0u);
+  if (!narrow) {   // combine the waves' sums
+    if (lane() == 0) {
+      sh.pl_red[t >> 6] = total | ((uint64_t)n_long << 40);   // rows < 2^23
+      sh.pl_red2[t >> 6] = tiles;
+    }
+    __syncthreads();
+    uint64_t packed = 0;
+    tiles = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    packed += sh.pl_red[i];
-    tiles += sh.pl_red2[i];
+    for (int i = 0; i < kWaves; ++i) {
+      packed += sh.pl_red[i];
+      tiles += sh.pl_red2[i];
+    }
+    total = packed & ((1ull << 40) - 1);
+    n_long = (int32_t)(packed >> 40);
   }
-  const uint64_t total = packed & ((1ull << 40) - 1);
-  const int32_t n_long = (int32_t)(packed >> 40);
   int64_t c;
-  const int g = t < R ? split_of(len, plan_args_of(a), total, n_long, tiles, &c) : 0;
+  const int g = r < R ? split_of(len, plan_args_of(a), total, n_long, tiles, &c) : 0;
   // One scan of three packed counts: split items (12 bits: at most the
   // grid, which the host keeps below 4096 for this path), split rows and
   // whole rows (10 bits each: at most kInKernelPlanRows).
   const uint32_t packed_n = (g > 1 ? (uint32_t)g | (1u << 12) : 0u) | (g == 1 ? 1u << 22 : 0u);
-  uint32_t packed_tot;
-  const uint32_t packed_off = block_exclusive_add(packed_n, sh.scratch, &packed_tot);
+  uint32_t packed_tot, packed_off;
+  if (narrow) {
+    const uint32_t inc = wave_inclusive_add(packed_n);
+    packed_off = inc - packed_n;
+    packed_tot = (uint32_t)__builtin_amdgcn_readlane((int)inc, kWave - 1);
+  } else {
+    packed_off = block_exclusive_add(packed_n, sh.scratch, &packed_tot);
+  }
+  // The items are written by threads t < R, which hold row t either way
+  // (narrow: R <= kWave puts them all in wave 0, where r == t).
   const uint32_t off_m = packed_off & 0xFFFu, off_g = (packed_off >> 12) & 0x3FFu, off_s = packed_off >> 22;
   const uint32_t tot_m = packed_tot & 0xFFFu, tot_g = (packed_tot >> 12) & 0x3FFu, tot_s = packed_tot >> 22;
   const int G = (int)gridDim.x, B = (int)blockIdx.x;
@@ -1696,7 +1720,8 @@ __device__ __forceinline__ bool guess_and_plan(const SelectArgs& a, Smem& sh, in
   int32_t len_t = 0;
   if constexpr (OVERLAP > 0) {
     // (loads complete in order: waiting for the length does not wait for the tile)
-    len_t = (int)threadIdx.x < a.num_rows ? a.lengths[threadIdx.x] : 0;
+    const int r = (int)threadIdx.x & (a.num_rows <= kWave ? kWave - 1 : kBlock - 1);   // as plan_here reads it
+    len_t = r < a.num_rows ? a.lengths[r] : 0;
     asm volatile("" ::: "memory");
   }
   float4 x[kEpt / 4];
@@ -1729,7 +1754,10 @@ __device__ __forceinline__ bool guess_and_plan(const SelectArgs& a, Smem& sh, in
   }
   // (the barriers of the planning order this clear before any histogram add)
   if (srow >= 0) hist_copies_clear(reinterpret_cast<uint32_t*>(sh.list));
-  if constexpr (OVERLAP == 0) len_t = (int)threadIdx.x < a.num_rows ? a.lengths[threadIdx.x] : 0;
+  if constexpr (OVERLAP == 0) {
+    const int r = (int)threadIdx.x & (a.num_rows <= kWave ? kWave - 1 : kBlock - 1);   // as plan_here reads it
+    len_t = r < a.num_rows ? a.lengths[r] : 0;
+  }
   num_items = plan_here(a, sh, len_t);
   if constexpr (OVERLAP > 0) {
     // Keep the tile's first use here: the compiler would otherwise convert
@@ -1749,7 +1777,8 @@ __device__ __forceinline__ bool guess_and_plan(const SelectArgs& a, Smem& sh, in
     parked = w0.row == srow && w0.begin == sbeg && end0 <= send && w0.len > a.k && (int64_t)w0.len <= a.max_len;
     if (parked) {
       uint32_t hk[kHk];
-      pack_hist(x, sbeg, end0, hk, reinterpret_cast<uint32_t*>(sh.list));
+      // (OVERLAP > 0: a guessed chunk spans at most OVERLAP vector groups)
+      pack_hist<(OVERLAP > 0 ? OVERLAP : kEpt / 4)>(x, sbeg, end0, hk, reinterpret_cast<uint32_t*>(sh.list));
       uint32_t* pt = parked_tile(sh);
 #pragma unroll
       for (int i = 0; i < kHk; ++i) pt[i * kBlock + threadIdx.x] = hk[i];

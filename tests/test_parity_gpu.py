@@ -276,6 +276,21 @@ def test_guessed_tile_paths(max_len, exact, alphabet):
         _gpu.assert_matches_oracle(w, got, f"guessed tile {max_len}")
 
 
+@pytest.mark.parametrize("rows,max_len,exact", [
+    (1, 90_000, True), (63, 40_000, False), (64, 40_000, True), (65, 40_000, True), (65, 40_000, False),
+    (130, 12_000, False),
+], ids=["1-row", "63-ragged", "64", "65", "65-ragged", "130-ragged"])
+def test_in_kernel_plan_across_the_one_wave_boundary(rows, max_len, exact):
+    """In-kernel planning reduces and scans the row lengths inside each wave
+    while the batch has at most 64 rows, and across the workgroup's waves
+    above that: both sides of the switch, with split rows (lengths beyond one
+    register tile) and ragged lengths, must give the oracle's result."""
+    w = synth.random_case(900 + rows, rows, max_len, exact_len=exact, alphabet=0)
+    _gpu.say(f"[plan boundary] {rows} rows, max_len {max_len}, exact {exact}")
+    for got in _gpu.run_gpu(w, "auto", repeat=2):
+        _gpu.assert_matches_oracle(w, got, f"plan boundary {rows}")
+
+
 @pytest.mark.parametrize("n", [0, 3, 4, 1_000_003, 7_000_000])
 def test_stream_read_hook_reads_every_vector(n):
     """The read-ceiling hook reads each 16-byte vector of x exactly once: its
