@@ -469,7 +469,7 @@ __device__ __forceinline__ void load_pack(const float* rowp, int32_t base, int32
 // all 256 scores of a wave's dwordx4 (all-equal or one-bin rows), a single
 // atomic adds 256. NaN padding lands in an unscanned bin; dwordx4 groups
 // wholly past `end` are skipped (the test is uniform across the workgroup).
-constexpr int kHistCopies = 16;
+constexpr int kHistCopies = 8;   // (16 measured slower: more LDS to clear and sum)
 static_assert(kBins * kHistCopies * 4 <= kListCap * 8, "histogram copies fit in the LDS list region");
 
 // Pack a tile (as pack_tile) and bin it into the copies in one pass over the
