@@ -252,7 +252,7 @@ constexpr int kResolveRegs = 24;                    // candidates per lane of th
 // turns out lower, the workgroup re-reads from the tile instead. Up to
 // kPreRegs per lane; positions are listed in the top of the LDS list, values
 // and block-table entries held in registers.
-constexpr int kPreRegs = 8;
+constexpr int kPreRegs = 4;
 constexpr int kPreCap = kPreRegs * kBlock;
 constexpr int kStageCap = kListCap - kPreCap / 2;  // staged candidates below the position list
 static_assert(kWideWords * 4 <= kListCap * 8, "first-digit histogram aliases the LDS list");
