@@ -45,6 +45,14 @@ DESCRIPTIONS = {
 }
 
 
+HOST_THREADS_MAX = 16   # CPU share of one GPU on the measurement host, whatever nproc reports
+
+
+def host_threads(rows: int) -> int:
+    """Oracle threads for a batch: one row range each, at most the host share."""
+    return max(1, min(rows, HOST_THREADS_MAX, os.cpu_count() or 1))
+
+
 def say(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
@@ -61,7 +69,21 @@ def workload(name: str):
     table = {"7x1m": 3, "7x80k": 2, "c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5}
     if name == "cp8_7x125k":
         return synth.make_cp_shard()
+    if name == "prefill_4096x80k":
+        return synth.make_prefill()
+    if name == "plan_split_600":
+        return synth.make_plan_split()
     return synth.make_config(table[name])
+
+
+def row_sample(w, rows: int):
+    """The first `rows` rows of a workload (a bounded sample for the oracle)."""
+    import synth
+    if rows >= w.rows:
+        return w
+    bt = w.block_table if w.bt_row_stride == 0 else w.block_table[:rows]
+    return synth.Workload(w.name + f"_first{rows}", w.scores[:rows], w.lengths[:rows], bt,
+                          w.bt_row_stride, w.page_size, w.k, w.seed)
 
 
 def algorithmic_bytes(w, slots, with_idx: bool) -> int:
@@ -79,12 +101,16 @@ def algorithmic_bytes(w, slots, with_idx: bool) -> int:
     return 4 * n_scores + 4 * w.rows + 4 * n_table + outputs
 
 
+EVENT_STEPS_MIN = 200   # event-timed steps (outside the timed region) for percentiles
+
+
 def measure(w, steps: int, warmup: int, with_idx: bool = True, rotate: bool = True):
     """Time `steps` plan+select steps; returns a dict of timings and the last output.
 
-    Two passes of `steps` steps each. The first is the timed region proper:
-    nothing but the steps between two synchronisations (wall clock per step).
-    The second records HIP events: stream events around the planning kernel
+    Two passes. The first is the timed region proper: exactly `steps` steps
+    and nothing else between two synchronisations (wall clock per step). The
+    second, max(steps, 200) steps so that the percentiles rest on enough
+    launches, records HIP events: stream events around the planning kernel
     and the selection call, on the stream both are launched on (torch's current
     stream, which the binding passes to the library), and the selection
     kernel's own start and end (topk_select_paged_timed), the interval a
@@ -120,7 +146,8 @@ def measure(w, steps: int, warmup: int, with_idx: bool = True, rotate: bool = Tr
 
     for i in range(warmup):
         step(i)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    n_ev = max(steps, EVENT_STEPS_MIN)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_ev)]
     for e in evs:   # create the kernel-event pair's HIP events before timing
         e[3].record(stream)
         e[4].record(stream)
@@ -130,7 +157,7 @@ def measure(w, steps: int, warmup: int, with_idx: bool = True, rotate: bool = Tr
         step(warmup + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    for i in range(steps):
+    for i in range(n_ev):
         step(warmup + steps + i, evs[i])
     torch.cuda.synchronize()
     st = tk.status()
@@ -139,7 +166,7 @@ def measure(w, steps: int, warmup: int, with_idx: bool = True, rotate: bool = Tr
     plan_ms = [e[0].elapsed_time(e[1]) for e in evs]
     sel_ms = [e[3].elapsed_time(e[4]) for e in evs]
     sel_stream_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    last = (warmup + 2 * steps - 1) % ncopy
+    last = (warmup + steps + n_ev - 1) % ncopy
     out = (None if idx is None else idx.cpu().numpy(), slots.cpu().numpy())
     res = {
         "ms_per_step": (t1 - t0) * 1e3 / steps,
@@ -148,6 +175,8 @@ def measure(w, steps: int, warmup: int, with_idx: bool = True, rotate: bool = Tr
         "select_p10_ms": float(np.percentile(sel_ms, 10)),
         "select_p90_ms": float(np.percentile(sel_ms, 90)),
         "plan_ms": float(np.mean(plan_ms)),
+        "plan_p50_ms": float(np.median(plan_ms)),
+        "event_steps": n_ev,
         "select_stream_ms": float(np.mean(sel_stream_ms)),
         "copies": ncopy,
         "out": out,
@@ -208,9 +237,12 @@ def read_ceiling(headline_bytes: int, reps: int = 20) -> dict:
 
 
 def cpu_baseline(w, seconds: float):
-    """The oracle as it stands, over whole batches, until `seconds` have passed."""
+    """The oracle as it stands, over whole batches: with one thread per row
+    range (min(rows, nproc) threads) until `seconds` have passed, and with a
+    single thread (median of 3 batches). Returns the record and the oracle's
+    result on the batch."""
     import oracle
-    threads = min(w.rows, os.cpu_count() or 1)
+    threads = host_threads(w.rows)
     reps = 0
     t0 = time.perf_counter()
     result = None
@@ -220,9 +252,16 @@ def cpu_baseline(w, seconds: float):
         if time.perf_counter() - t0 >= seconds or reps >= 50:
             break
     dt = time.perf_counter() - t0
+    one = []
+    for _ in range(3):
+        t = time.perf_counter()
+        oracle.topk_workload(w, threads=1)
+        one.append(time.perf_counter() - t)
     return {"value": round(dt / reps * 1e6, 1), "unit": "µs", "cores": threads, "kind": "oracle",
             "sample": f"{reps} full batches of {w.rows}x{w.stride} (full sort per row, "
-                      f"{threads} threads, one row range each)"}, result
+                      f"{threads} threads, one row range each); one thread: median of 3 batches",
+            "one_thread_value": round(statistics.median(one) * 1e6, 1),
+            "nproc": os.cpu_count(), "cpu_model": cpu_model()}, result
 
 
 def matches(got, want) -> bool:
@@ -252,16 +291,20 @@ def sweep(args) -> int:
         w = workload(name)
         say(f"[bench] sweep {name}: {w.rows}x{w.stride}")
         res = measure(w, args.steps, args.warmup, rotate=not args.warm_cache)
-        nthreads = min(w.rows, os.cpu_count() or 1)
+        nthreads = host_threads(w.rows)
+        # the oracle's timing on at most 256 rows (scaled to the batch); its
+        # parity result on the whole batch
+        ws = row_sample(w, 256)
         t1, tn = [], []
-        ref = None
         for _ in range(3):
             t = time.perf_counter()
-            ref = oracle.topk_workload(w, threads=1)
+            oracle.topk_workload(ws, threads=1)
             t1.append(time.perf_counter() - t)
             t = time.perf_counter()
-            oracle.topk_workload(w, threads=nthreads)
+            oracle.topk_workload(ws, threads=min(ws.rows, nthreads))
             tn.append(time.perf_counter() - t)
+        scale = w.rows / ws.rows
+        ref = oracle.topk_workload(w, threads=nthreads) if ws is not w else oracle.topk_workload(w, threads=1)
         parity = matches(res["out"], ref) and res["last_copy_equal"]
         ok &= parity
         nbytes = algorithmic_bytes(w, res["out"][1], True)
@@ -270,13 +313,16 @@ def sweep(args) -> int:
             "workload": w.name, "rows": w.rows, "stride": w.stride, "k": w.k,
             "select_us": {"p50": round(res["select_p50_ms"] * 1e3, 3), "p10": round(res["select_p10_ms"] * 1e3, 3),
                           "p90": round(res["select_p90_ms"] * 1e3, 3), "mean": round(res["select_ms"] * 1e3, 3)},
-            "plan_us": round(res["plan_ms"] * 1e3, 3) if w.rows > IN_KERNEL_PLAN_ROWS else "in-kernel",
+            "plan_us": ({"mean": round(res["plan_ms"] * 1e3, 3), "p50": round(res["plan_p50_ms"] * 1e3, 3)}
+                        if w.rows > IN_KERNEL_PLAN_ROWS else "in-kernel"),
             "step_us": round(res["ms_per_step"] * 1e3, 3),
             "rows_per_s": round(w.rows / p50), "algorithmic_bytes": nbytes,
             "gbs": round(nbytes / p50 / 1e9, 1), "frac_of_8tbs": round(nbytes / p50 / 1e9 / PEAK_HBM_GBS, 4),
             "cache": "warm" if args.warm_cache else f"cold ({res['copies']} copies)",
-            "oracle_1thread_s": round(statistics.median(t1), 4),
-            f"oracle_{nthreads}threads_s": round(statistics.median(tn), 4),
+            "oracle_1thread_s": round(statistics.median(t1) * scale, 4),
+            f"oracle_{min(ws.rows, nthreads)}threads_s": round(statistics.median(tn) * scale, 4),
+            "oracle_sample": (f"first {ws.rows} of {w.rows} rows, scaled by {scale:g}" if ws is not w
+                              else "whole batch, median of 3"),
             "cpu": cpu_model(), "nproc": os.cpu_count(), "parity": parity,
         }), flush=True)
     return 0 if ok else 1
@@ -297,7 +343,8 @@ def main() -> int:
     ap.add_argument("--no-read-ceiling", action="store_true",
                     help="skip the streaming-read ceiling measurement")
     ap.add_argument("--sweep", default="",
-                    help="comma list from {c1..c5, cp8_7x125k}: one JSON line per workload")
+                    help="comma list from {c1..c5, cp8_7x125k, prefill_4096x80k, plan_split_600}: "
+                         "one JSON line per workload")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -329,7 +376,7 @@ def main() -> int:
         say(f"[bench] oracle CPU baseline on {head} for ~{args.cpu_seconds:g} s")
         base, ref = cpu_baseline(w, args.cpu_seconds)
     else:
-        ref = oracle.topk_workload(w, threads=min(w.rows, os.cpu_count() or 1))
+        ref = oracle.topk_workload(w, threads=host_threads(w.rows))
     parity = matches(res["out"], ref) and res["last_copy_equal"]
 
     nbytes = algorithmic_bytes(w, res["out"][1], True)
@@ -350,7 +397,7 @@ def main() -> int:
         "ms_per_step": round(res["ms_per_step"], 6),
         "higher_is_better": False,
         "scaling": "weak",
-        "vs_baseline": round(step_us / PAGES_V2_US[head], 4),
+        "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
         "config": {
@@ -372,8 +419,10 @@ def main() -> int:
             "kernel_us": round(res["select_ms"] * 1e3, 3),
         },
         "cpu_baseline": base,
+        "vs_oracle": round(base["value"] / step_us, 1) if base else None,
         "hbm_read_ceiling": ceiling,
-        "select_us": {"mean": round(res["select_ms"] * 1e3, 3), "p10": round(res["select_p10_ms"] * 1e3, 3),
+        "select_us": {"event_steps": res["event_steps"],
+                      "mean": round(res["select_ms"] * 1e3, 3), "p10": round(res["select_p10_ms"] * 1e3, 3),
                       "p50": round(res["select_p50_ms"] * 1e3, 3), "p90": round(res["select_p90_ms"] * 1e3, 3),
                       "stream_events_mean": round(res["select_stream_ms"] * 1e3, 3)},
         "plan_us": round(res["plan_ms"] * 1e3, 3) if w.rows > IN_KERNEL_PLAN_ROWS else None,
@@ -384,12 +433,15 @@ def main() -> int:
     ok = parity
     for n in names[1:]:
         w2, r2 = results[n]
-        p2 = matches(r2["out"], oracle.topk_workload(w2, threads=min(w2.rows, os.cpu_count() or 1)))
+        p2 = matches(r2["out"], oracle.topk_workload(w2, threads=host_threads(w2.rows)))
         ok &= p2
         line[f"latency_{n}_us"] = {"step": round(r2["ms_per_step"] * 1e3, 3),
                                    "select_mean": round(r2["select_ms"] * 1e3, 3),
                                    "select_stream_events_mean": round(r2["select_stream_ms"] * 1e3, 3),
                                    "select_p50": round(r2["select_p50_ms"] * 1e3, 3),
+                                   "select_p10": round(r2["select_p10_ms"] * 1e3, 3),
+                                   "select_p90": round(r2["select_p90_ms"] * 1e3, 3),
+                                   "event_steps": r2["event_steps"],
                                    "plan": round(r2["plan_ms"] * 1e3, 3) if w2.rows > IN_KERNEL_PLAN_ROWS
                                    else "in the selection kernel", "parity": p2}
     print(json.dumps(line), flush=True)

@@ -48,6 +48,26 @@
  *   the block table covers ceil(lengths[r] / page_size) pages with entries >= 0,
  *   and every slot page * page_size + page_size - 1 fits in int32;
  *   the lengths given to topk_select_paged equal those the plan was built from.
+ *
+ * Split rows
+ * ----------
+ * The page splits a long row across an 8-CTA thread-block cluster and reduces
+ * the CTAs' histograms across the cluster (Figure 2 caption). gfx950 has no
+ * clusters: the library splits a long row across G workgroups of one
+ * persistent grid, which merge their histograms through global atomics and then
+ * wait for one another at a bounded spin barrier in device memory. That wait
+ * is only guaranteed to end if every workgroup of the selection grid is
+ * resident on the device at the same time. The library sizes the grid to the
+ * device's co-resident capacity for one 512-lane workgroup per compute unit
+ * (topk_query_sizes) and puts every split row's chunks in the grid's first
+ * round, so an otherwise idle device always satisfies this. Work that other
+ * streams or processes run on the device at the same time can occupy compute
+ * units and delay some of the grid's workgroups; the split rows' workgroups
+ * that started then poll until cfg->spin_limit runs out, set
+ * TOPK_DEVICE_SPIN_TIMEOUT in the workspace status word and exit (the kernel
+ * always ends). Those rows' outputs are then incomplete and the workspace
+ * must be cleared with topk_workspace_init before its next use. The caller
+ * sees this only through topk_read_status; it never hangs the device.
  */
 #ifndef SPARSE_TOPK_H
 #define SPARSE_TOPK_H
@@ -59,14 +79,17 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* Status codes. A plain int32 rather than an enum type, so that any value a
+ * caller passes back (topk_status_string) is a valid value of the type. */
+typedef int32_t topk_status;
+enum {
   TOPK_OK = 0,
   TOPK_ERR_INVALID_ARG = -1,     /* a host-checkable argument is out of range or NULL */
   TOPK_ERR_BUFFER_TOO_SMALL = -2,/* plan or workspace smaller than topk_query_sizes says */
   TOPK_ERR_UNSUPPORTED = -3,     /* forced path cannot serve the configured rows */
   TOPK_ERR_HIP = -4,             /* a HIP runtime call or kernel launch failed */
   TOPK_ERR_DEVICE = -5           /* topk_read_status: the device recorded an error */
-} topk_status;
+};
 
 /* Path selection (tests and tuning). AUTO lets the planner choose per row. */
 enum {
@@ -86,17 +109,23 @@ typedef struct {
   int32_t cand_capacity;  /* 0 = default; > 0 caps the per-row boundary-candidate buffer
                              (rows whose boundary bin holds more use a re-streaming path) */
   int32_t min_chunk;      /* 0 = default; > 0 smallest chunk (elements) the planner splits to */
-  int32_t reserved[4];    /* must be zero */
+  int32_t spin_limit;     /* bound on the split-row wait (see "Split rows" above):
+                             0 = default (2^21 polls, about 1 s); > 0 = at most this many polls;
+                             -1 = give up without polling (tests the time-out path); else invalid */
+  int32_t reserved[3];    /* must be zero */
 } topk_config;
 
 /*
  * Host only. Sizes in bytes of the plan buffer (written by topk_plan) and the
  * workspace (used by topk_select_paged) for `cfg` on the current HIP device.
  * Status: OK, INVALID_ARG (bad cfg or NULL outputs), HIP (device query failed).
+ * Passage: none; the pages define no buffers. This is the library's own sizing
+ * of the plan and the cross-workgroup state that replace the page's cluster.
  */
 topk_status topk_query_sizes(const topk_config* cfg, size_t* plan_bytes, size_t* workspace_bytes);
 
 /*
+ * Passage: none (the library's own state, see "Split rows").
  * Enqueue a fill kernel that zeroes `workspace`. Required once before the
  * first topk_select_paged on a workspace, and again after topk_read_status
  * reports TOPK_ERR_DEVICE. topk_select_paged leaves the workspace zeroed for
@@ -141,6 +170,7 @@ topk_status topk_select_paged(const topk_config* cfg, const void* plan,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Passage: TopK-V2 text and Figure 4 (the kernel latency the page measures).
  * topk_select_paged for measurement: identical arguments, results and errors,
  * plus two HIP events (hipEvent_t, created by the caller, timing enabled)
  * that record the selection kernel's own start and end, as a kernel trace
@@ -157,6 +187,7 @@ topk_status topk_select_paged_timed(const topk_config* cfg, const void* plan,
                                     void* start_event, void* stop_event);
 
 /*
+ * Passage: none (the library's error reporting).
  * SYNCHRONISES `stream`. Copies the device status word of `workspace` into
  * *host_status (host pointer): 0, or a bitwise OR of TOPK_DEVICE_* flags.
  * Returns TOPK_ERR_DEVICE when the word is non-zero.
@@ -170,7 +201,9 @@ enum {
 topk_status topk_read_status(const void* workspace, size_t workspace_bytes,
                              int32_t* host_status, void* stream);
 
-/* Elements one workgroup holds in registers (the register path's row limit). */
+/* Elements one workgroup holds in registers (the register path's row limit).
+ * Passage: TopK-V2 text, the register-resident path for short rows; the
+ * limit itself is this library's tile size. */
 int64_t topk_register_capacity(void);
 
 /*
@@ -186,6 +219,33 @@ int64_t topk_register_capacity(void);
 topk_status topk_debug_keys(const float* x, int64_t n, uint32_t* bin_out, uint32_t* key32_out, void* stream);
 
 /*
+ * Test hook for the coarse histogram and threshold bin (page: TopK-V2,
+ * Figure 3 caption: each score's FP16 key selects one of 1,024 bins by its
+ * upper 10 bits and the bin's counter is incremented; Figure 2 caption: the
+ * reduction locates the bin holding the k-th largest score). For each row r
+ * of scores (device, float[num_rows][score_row_stride], valid prefix
+ * lengths[r] (device), 0 <= lengths[r] <= score_row_stride) it writes, with
+ * the selection kernel's own binning and threshold scan:
+ *   hist_out[r * 1024 + b]   scores of the valid prefix in ordered bin b
+ *                            (device, uint32[num_rows][1024]); bins 15 (-inf)
+ *                            to 1008 (+inf) hold every non-NaN score; bins
+ *                            0-14 and 1009-1023 hold only NaN codes, and the
+ *                            kernel counts its padding of a tile past the
+ *                            row's end there (it never scans them);
+ *   threshold_out[r * 3 + 0..2] = { b*, scores in bins above b*, scores in b* }
+ *                            (device, uint32[num_rows][3]): b* is the bin with
+ *                            above(b*) < k <= above(b*) + hist[b*]; for rows of
+ *                            at most k scores, { 0xFFFFFFFF, 0, 0 }.
+ * 1 <= k <= 2048. One workgroup per row; enqueued on `stream`. Status: OK,
+ * INVALID_ARG (bad k, num_rows < 0, NULL pointer with num_rows > 0), HIP.
+ */
+topk_status topk_debug_histogram(const float* scores, int64_t score_row_stride, const int32_t* lengths,
+                                 int32_t num_rows, int32_t k, uint32_t* hist_out, uint32_t* threshold_out,
+                                 void* stream);
+
+/*
+ * Passage: none; a measurement aid for the roofline of the streaming step
+ * (TopK-V2 text: each score row is read once).
  * Measurement hook: the device's streaming-read ceiling for this access
  * pattern. Reads the whole 16-byte vectors of x[0, n) (device, n >= 0,
  * 16-byte aligned) once with the selection kernel's loads (512-lane
@@ -199,8 +259,11 @@ topk_status topk_debug_keys(const float* x, int64_t n, uint32_t* bin_out, uint32
  */
 topk_status topk_debug_stream_read(const float* x, int64_t n, float* out, void* stream, void* start_event,
                                    void* stop_event);
+/* Partial sums topk_debug_stream_read writes (its grid). Passage: none. */
 int32_t topk_stream_read_groups(void);
 
+/* Passage: none. A static string describing `s` ("unknown status" for values
+ * outside topk_status); never NULL, owned by the library. */
 const char* topk_status_string(topk_status s);
 
 #ifdef __cplusplus

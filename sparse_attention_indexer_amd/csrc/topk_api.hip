@@ -22,6 +22,8 @@ hipError_t select_occupancy(int* per_cu);
 hipError_t launch_stream_read(const float* x, int64_t n, float* out, hipStream_t s, hipEvent_t start,
                               hipEvent_t stop);
 int stream_read_groups();
+hipError_t launch_debug_hist(const float* scores, int64_t stride, const int32_t* lengths, int32_t rows, int32_t k,
+                             uint32_t* hist, uint32_t* res, hipStream_t s);
 }  // namespace satopk
 
 using namespace satopk;
@@ -66,7 +68,8 @@ topk_status check_config(const topk_config* cfg) {
   if (cfg->force_path < TOPK_PATH_AUTO || cfg->force_path > TOPK_PATH_MULTI) return TOPK_ERR_INVALID_ARG;
   if (cfg->wg_per_row < 0 || cfg->wg_per_row == 1) return TOPK_ERR_INVALID_ARG;
   if (cfg->cand_capacity < 0 || cfg->min_chunk < 0) return TOPK_ERR_INVALID_ARG;
-  for (int i = 0; i < 4; ++i)
+  if (cfg->spin_limit < -1) return TOPK_ERR_INVALID_ARG;
+  for (int i = 0; i < 3; ++i)
     if (cfg->reserved[i] != 0) return TOPK_ERR_INVALID_ARG;
   if (cfg->force_path == TOPK_PATH_REGISTER && cfg->max_len > kTile) return TOPK_ERR_UNSUPPORTED;
   return TOPK_OK;
@@ -176,6 +179,17 @@ topk_status topk_plan(const topk_config* cfg, const int32_t* lengths, int32_t nu
 
 namespace {
 
+// Host-checkable arguments of a selection call (beyond the configuration).
+bool select_args_ok(const topk_config* cfg, int64_t score_row_stride, int32_t num_rows, const float* scores,
+                    const int32_t* lengths, const int32_t* block_table, int64_t bt_row_stride, int32_t page_size,
+                    const int32_t* out_slots, int64_t out_row_stride) {
+  if (num_rows < 0 || num_rows > cfg->max_rows) return false;
+  if (page_size < 1 || bt_row_stride < 0 || out_row_stride < cfg->k) return false;
+  if (score_row_stride < cfg->max_len || score_row_stride < 0) return false;
+  if (num_rows > 0 && (!scores || !lengths || !block_table || !out_slots)) return false;
+  return true;
+}
+
 topk_status select_impl(const topk_config* cfg, const void* plan, const float* scores, int64_t score_row_stride,
                         const int32_t* lengths, int32_t num_rows, const int32_t* block_table, int64_t bt_row_stride,
                         int32_t page_size, int32_t* out_slots, int32_t* out_indices, int64_t out_row_stride,
@@ -184,11 +198,10 @@ topk_status select_impl(const topk_config* cfg, const void* plan, const float* s
   Sizing s;
   const topk_status st = sizing(cfg, &s);
   if (st != TOPK_OK) return st;
-  if (num_rows < 0 || num_rows > cfg->max_rows) return TOPK_ERR_INVALID_ARG;
-  if (page_size < 1 || bt_row_stride < 0 || out_row_stride < cfg->k) return TOPK_ERR_INVALID_ARG;
-  if (score_row_stride < cfg->max_len || score_row_stride < 0) return TOPK_ERR_INVALID_ARG;
+  if (!select_args_ok(cfg, score_row_stride, num_rows, scores, lengths, block_table, bt_row_stride, page_size,
+                      out_slots, out_row_stride))
+    return TOPK_ERR_INVALID_ARG;
   if ((!plan && (num_rows > kInKernelPlanRows || s.grid >= 4096)) || !workspace) return TOPK_ERR_INVALID_ARG;
-  if (num_rows > 0 && (!scores || !lengths || !block_table || !out_slots)) return TOPK_ERR_INVALID_ARG;
   if (workspace_bytes < s.workspace_bytes) return TOPK_ERR_BUFFER_TOO_SMALL;
   if (num_rows == 0) return TOPK_OK;
   SelectArgs a;
@@ -221,7 +234,7 @@ topk_status select_impl(const topk_config* cfg, const void* plan, const float* s
   a.cand_cap = s.cand_cap;
   a.status = (int32_t*)workspace;
   a.max_len = cfg->max_len;
-  a.spin_limit = kDefaultSpinLimit;
+  a.spin_limit = cfg->spin_limit == 0 ? kDefaultSpinLimit : cfg->spin_limit < 0 ? 0u : (uint32_t)cfg->spin_limit;
   // The selection kernel starts loading its tile before the lengths arrive,
   // guessing that every row has max_len scores; the guess is the planner's
   // own split of such a batch.
@@ -295,6 +308,7 @@ topk_status topk_read_status(const void* workspace, size_t workspace_bytes, int3
 
 int64_t topk_register_capacity(void) { return kTile; }
 
+
 topk_status topk_debug_keys(const float* x, int64_t n, uint32_t* bin_out, uint32_t* key32_out, void* stream) {
   if (n < 0 || (n > 0 && !x)) return TOPK_ERR_INVALID_ARG;
   return launch_debug_keys(x, n, bin_out, key32_out, (hipStream_t)stream) == hipSuccess
@@ -314,6 +328,17 @@ topk_status topk_debug_stream_read(const float* x, int64_t n, float* out, void* 
 }
 
 int32_t topk_stream_read_groups(void) { return stream_read_groups(); }
+
+topk_status topk_debug_histogram(const float* scores, int64_t score_row_stride, const int32_t* lengths,
+                                 int32_t num_rows, int32_t k, uint32_t* hist_out, uint32_t* threshold_out,
+                                 void* stream) {
+  if (num_rows < 0 || k < 1 || k > kMaxK || score_row_stride < 0) return TOPK_ERR_INVALID_ARG;
+  if (num_rows > 0 && (!scores || !lengths || !hist_out || !threshold_out)) return TOPK_ERR_INVALID_ARG;
+  return launch_debug_hist(scores, score_row_stride, lengths, num_rows, k, hist_out, threshold_out,
+                           (hipStream_t)stream) == hipSuccess
+             ? TOPK_OK
+             : TOPK_ERR_HIP;
+}
 
 const char* topk_status_string(topk_status s) {
   switch (s) {

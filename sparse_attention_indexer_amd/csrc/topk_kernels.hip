@@ -1346,21 +1346,20 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
   // read every final value: a consistent snapshot of the merge.
   {
     static_assert(kBins == 2 * kBlock, "two bins per lane");
-    uint32_t spins = 0;
-    bool ok = true;
-    for (;;) {
+    // At most spin_limit polls (uniform); a limit of 0 gives up at once.
+    bool ok = false;
+    for (uint32_t spins = 0; spins < a.spin_limit; ++spins) {
       const uint32_t h0 = ld_agent(&g->hist[t]), h1 = ld_agent(&g->hist[t + kBlock]);
       const uint32_t rest = t == 0 ? ld_agent(&g->arrive) : 0u;
       sh.rhist[t] = h0;
       sh.rhist[t + kBlock] = h1;
       uint32_t tot;
       block_exclusive_add(h0 + h1 + rest, sh.scratch, &tot);
-      if (uni(tot) == (uint32_t)len) break;
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > a.spin_limit) {
-        ok = false;
+      if (uni(tot) == (uint32_t)len) {
+        ok = true;
         break;
       }
+      __builtin_amdgcn_s_sleep(1);
     }
     if (!ok) {
       if (t == 0) atomicOr(a.status, TOPK_DEVICE_SPIN_TIMEOUT);
@@ -1843,6 +1842,45 @@ __global__ void topk_debug_keys_kernel(const float* x, int64_t n, uint32_t* bin,
   }
 }
 
+// The selection kernel's coarse histogram and threshold bin of each row, with
+// its own binning (pack_hist into interleaved copies, hist_copies_sum) and its
+// own threshold scan (find_threshold_raw). One workgroup per row; rows are
+// read in whole tiles with per-element loads (any alignment). Writes
+// hist[r][b] for ordered bins b (NaN-only bins included) and, for rows longer
+// than k, res[r] = {b*, scores above b*, scores in b*}; shorter rows get
+// {kNotFound, 0, 0}.
+struct __align__(16) DebugSmem {
+  uint32_t hc[kBins * kHistCopies];
+  uint32_t h[kBins];
+  uint32_t scratch[kWaves];
+  uint32_t res[4];
+};
+
+__global__ void __launch_bounds__(kBlock) topk_debug_hist_kernel(const float* scores, int64_t stride,
+                                                                  const int32_t* lengths, int32_t k,
+                                                                  uint32_t* hist, uint32_t* res) {
+  __shared__ DebugSmem sh;
+  const int r = blockIdx.x;
+  const int32_t len = lengths[r];
+  const float* rowp = scores + (int64_t)r * stride;
+  hist_copies_clear(sh.hc);
+  __syncthreads();
+  for (int32_t base = 0; base < len; base += kTile) {
+    float4 x[kEpt / 4];
+    uint32_t hk[kHk];
+    load_raw<false>(rowp, base, len, x);
+    pack_hist(x, base, len, hk, sh.hc);
+  }
+  __syncthreads();
+  hist_copies_sum(sh.hc, sh.h);
+  __syncthreads();
+  for (int b = threadIdx.x; b < kBins; b += kBlock) hist[(int64_t)r * kBins + b] = sh.h[raw_of_bin((uint32_t)b)];
+  if (threadIdx.x == 0) sh.res[0] = kNotFound, sh.res[1] = sh.res[2] = 0;
+  __syncthreads();
+  if (len > k) find_threshold_raw(sh.h, (uint32_t)k, sh.scratch, sh.res);
+  if (threadIdx.x < 3) res[(int64_t)r * 3 + threadIdx.x] = sh.res[threadIdx.x];
+}
+
 // Streaming-read ceiling: each workgroup reads its contiguous share of x with
 // the selection kernel's load pattern (lane t takes vector q * kBlock + t,
 // 16 vectors in flight) and writes one partial sum.
@@ -1944,6 +1982,13 @@ hipError_t launch_stream_read(const float* x, int64_t n, float* out, hipStream_t
 }
 
 int stream_read_groups() { return kStreamReadGroups; }
+
+hipError_t launch_debug_hist(const float* scores, int64_t stride, const int32_t* lengths, int32_t rows, int32_t k,
+                             uint32_t* hist, uint32_t* res, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_debug_hist_kernel, dim3(rows), dim3(kBlock), 0, s, scores, stride, lengths, k, hist, res);
+  return hipGetLastError();
+}
 
 hipError_t select_occupancy(int* per_cu) {
   int a = 0, b = 0;

@@ -32,7 +32,7 @@ class topk_config(ctypes.Structure):
     _fields_ = [("k", ctypes.c_int32), ("max_rows", ctypes.c_int32), ("max_len", ctypes.c_int64),
                 ("force_path", ctypes.c_int32), ("wg_per_row", ctypes.c_int32),
                 ("cand_capacity", ctypes.c_int32), ("min_chunk", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 4)]
+                ("spin_limit", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
 
 
 class TopKError(RuntimeError):
@@ -64,6 +64,7 @@ def load_library():
         "topk_read_status": [V, S, ctypes.POINTER(I32), V],
         "topk_debug_keys": [V, I64, V, V, V],
         "topk_debug_stream_read": [V, I64, V, V, V, V],
+        "topk_debug_histogram": [V, I64, V, I32, I32, V, V, V],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
@@ -86,11 +87,12 @@ def _check(fn: str, st: int) -> None:
 
 
 def make_config(k: int, max_rows: int, max_len: int, force_path: int | str = PATH_AUTO,
-                wg_per_row: int = 0, cand_capacity: int = 0, min_chunk: int = 0) -> topk_config:
+                wg_per_row: int = 0, cand_capacity: int = 0, min_chunk: int = 0,
+                spin_limit: int = 0) -> topk_config:
     if isinstance(force_path, str):
         force_path = PATHS[force_path]
     return topk_config(int(k), int(max_rows), int(max_len), int(force_path), int(wg_per_row),
-                       int(cand_capacity), int(min_chunk), (ctypes.c_int32 * 4)())
+                       int(cand_capacity), int(min_chunk), int(spin_limit), (ctypes.c_int32 * 3)())
 
 
 def _stream(stream) -> int:
@@ -108,6 +110,15 @@ def _need(t: torch.Tensor, dtype, name: str) -> None:
         raise TypeError(f"{name} must be a {dtype} tensor on the GPU")
 
 
+def _check_layout(lengths: torch.Tensor, block_table: torch.Tensor | None = None) -> None:
+    """The library reads lengths as a dense int32 array and each block-table
+    row as consecutive entries; a strided view would be read as other data."""
+    if not lengths.is_contiguous():
+        raise ValueError("lengths must be contiguous")
+    if block_table is not None and block_table.dim() > 0 and block_table.stride(-1) != 1:
+        raise ValueError("block_table must have unit stride along pages")
+
+
 # --- functions with the C names ------------------------------------------------
 
 def topk_query_sizes(cfg: topk_config) -> tuple[int, int]:
@@ -123,6 +134,7 @@ def topk_workspace_init(workspace: torch.Tensor, stream=None) -> None:
 
 
 def topk_plan(cfg: topk_config, lengths: torch.Tensor, plan: torch.Tensor, stream=None) -> None:
+    _check_layout(lengths)
     _need(lengths, torch.int32, "lengths")
     _check("topk_plan", load_library().topk_plan(
         ctypes.byref(cfg), lengths.data_ptr(), lengths.numel(), plan.data_ptr(),
@@ -131,6 +143,7 @@ def topk_plan(cfg: topk_config, lengths: torch.Tensor, plan: torch.Tensor, strea
 
 def _select_args(cfg, plan, scores, lengths, block_table, bt_row_stride, page_size, out_slots, out_indices,
                  workspace, stream):
+    _check_layout(lengths, block_table)
     _need(scores, torch.float32, "scores")
     _need(lengths, torch.int32, "lengths")
     _need(block_table, torch.int32, "block_table")
@@ -146,10 +159,10 @@ def _select_args(cfg, plan, scores, lengths, block_table, bt_row_stride, page_si
     rows = lengths.numel()
     if scores.shape[0] < rows or out_slots.shape[0] < rows:
         raise ValueError("scores and out_slots need a row per length")
-    return (ctypes.byref(cfg), plan.data_ptr(), scores.data_ptr(), scores.stride(0), lengths.data_ptr(), rows,
+    return (ctypes.byref(cfg), _ptr(plan), scores.data_ptr(), scores.stride(0), lengths.data_ptr(), rows,
             block_table.data_ptr(), int(bt_row_stride), int(page_size), out_slots.data_ptr(),
-            _ptr(out_indices), out_slots.stride(0), workspace.data_ptr(),
-            workspace.numel() * workspace.element_size(), _stream(stream))
+            _ptr(out_indices), out_slots.stride(0), _ptr(workspace),
+            0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream))
 
 
 def topk_select_paged(cfg: topk_config, plan: torch.Tensor, scores: torch.Tensor, lengths: torch.Tensor,
@@ -204,6 +217,23 @@ def topk_debug_keys(x: torch.Tensor, stream=None) -> tuple[torch.Tensor, torch.T
     return bins, keys
 
 
+def topk_debug_histogram(scores: torch.Tensor, lengths: torch.Tensor, k: int, stream=None):
+    """The selection kernel's coarse histogram (int32 [rows, 1024], ordered
+    bins) and threshold (int32 [rows, 3]: b*, above, count) of each row."""
+    _check_layout(lengths)
+    _need(scores, torch.float32, "scores")
+    _need(lengths, torch.int32, "lengths")
+    if scores.dim() != 2 or scores.stride(1) != 1:
+        raise ValueError("scores must be 2-D with unit stride along positions")
+    rows = lengths.numel()
+    hist = torch.empty((rows, 1024), dtype=torch.int32, device=scores.device)
+    thr = torch.empty((rows, 3), dtype=torch.int32, device=scores.device)
+    _check("topk_debug_histogram", load_library().topk_debug_histogram(
+        scores.data_ptr(), scores.stride(0), lengths.data_ptr(), rows, int(k), hist.data_ptr(),
+        thr.data_ptr(), _stream(stream)))
+    return hist, thr
+
+
 def topk_debug_stream_read(x: torch.Tensor, out: torch.Tensor | None = None, stream=None,
                            events=None) -> torch.Tensor:
     """One streaming read of ``x`` (float32, contiguous, 16-byte aligned) with
@@ -226,9 +256,11 @@ class TopK:
     """Owns a plan and a workspace sized for one configuration on one device."""
 
     def __init__(self, k: int, max_rows: int, max_len: int, *, force_path: int | str = PATH_AUTO,
-                 wg_per_row: int = 0, cand_capacity: int = 0, min_chunk: int = 0, device=None):
+                 wg_per_row: int = 0, cand_capacity: int = 0, min_chunk: int = 0, spin_limit: int = 0,
+                 device=None):
         self.device = torch.device("cuda" if device is None else device)
-        self.cfg = make_config(k, max_rows, max_len, force_path, wg_per_row, cand_capacity, min_chunk)
+        self.cfg = make_config(k, max_rows, max_len, force_path, wg_per_row, cand_capacity, min_chunk,
+                               spin_limit)
         with torch.cuda.device(self.device):
             plan_bytes, ws_bytes = topk_query_sizes(self.cfg)
             self.plan_buf = torch.zeros((plan_bytes + 15) // 16 * 4, dtype=torch.int32, device=self.device)

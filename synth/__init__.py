@@ -248,6 +248,57 @@ def make_cp_shard(seed: int = 6) -> Workload:
     return Workload("cp8_7x125k_shard", scores, lengths, bt, 0, ps, k, seed)
 
 
+def make_prefill(rows: int = 4096, prefix: int = 80_000, seed: int = 7) -> Workload:
+    """A prefill chunk of one request: ``rows`` query tokens whose causal rows
+    see ``prefix + t`` positions (t = 0 .. rows-1), N(0,1) scores, -inf past
+    each row's length, one shared random page table of 64-token pages.
+    This is the ragged prefill top-k the lmsys.org page lists as next work
+    (section "What's Next"), at its 80K context length.
+
+    At this size (344 M scores) Box-Muller per score would dominate the run,
+    so scores are drawn from a table of 2^20 N(0,1) values, two 20-bit table
+    indices per SplitMix64 output (bits 44-63 and 12-31). Values then repeat
+    within a row (about 3,400 equal pairs per 80K row), which also exercises
+    the position tie-break."""
+    ps, k = 64, 2048
+    lengths = (prefix + np.arange(rows)).astype(np.int32)
+    stride = int(lengths[-1]) + (-int(lengths[-1]) % 4) if rows else 4
+    scores = np.empty((rows, stride), np.float32)
+    table = _f32(Stream(seed, 5).normal(1 << 20))
+    block = 64
+    for r0 in range(0, rows, block):
+        r1 = min(rows, r0 + block)
+        n = (r1 - r0) * stride
+        u = Stream(seed, 1, r0).u64((n + 1) // 2)
+        idx = np.empty(2 * u.size, np.int64)
+        idx[0::2] = (u >> np.uint64(44)).astype(np.int64)
+        idx[1::2] = ((u >> np.uint64(12)) & np.uint64(0xFFFFF)).astype(np.int64)
+        scores[r0:r1] = table[idx[:n]].reshape(r1 - r0, stride)
+    for r in range(rows):
+        scores[r, lengths[r]:] = -np.inf
+    bt = page_permutation_tables(Stream(seed, 2), 1, (stride + ps - 1) // ps)
+    return Workload(f"prefill_{rows}x{prefix // 1000}k", scores, lengths, bt, 0, ps, k, seed)
+
+
+def make_plan_split(seed: int = 8, rows: int = 600, long_len: int = 300_000) -> Workload:
+    """More rows than the selection kernel plans by itself (so the planning
+    kernel writes the work list), four of them long enough to be split across
+    workgroups and the rest between k + 1 and 30,000 positions. Per-row
+    random page tables; N(0,1) scores, -inf padding."""
+    ps, k = 64, 2048
+    st = Stream(seed, 4)
+    lengths = (k + 1 + st.below(rows, 30_000 - k)).astype(np.int32)
+    long_rows = [rows // 8, 3 * rows // 8, 5 * rows // 8, 7 * rows // 8]
+    lengths[long_rows] = long_len
+    stride = long_len
+    scores = np.full((rows, stride), -np.inf, np.float32)
+    for r in range(rows):
+        scores[r, : lengths[r]] = _f32(Stream(seed, 1, r).normal(int(lengths[r])))
+    pages = (stride + ps - 1) // ps
+    bt = page_permutation_tables(Stream(seed, 2), rows, pages)
+    return Workload(f"plan_split_{rows}", scores, lengths, bt, pages, ps, k, seed)
+
+
 CONFIGS = {
     1: make_c1,
     2: make_c2,

@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
     for n in ("topk_query_sizes", "topk_plan", "topk_select_paged", "topk_workspace_init",
               "topk_read_status", "topk_status_string", "topk_register_capacity", "topk_debug_keys",
               "topk_debug_stream_read", "topk_stream_read_groups",
-              "topk_select_paged_timed"):
+              "topk_select_paged_timed", "topk_debug_histogram"):
         assert n in names
 
 
@@ -54,7 +54,7 @@ def test_register_capacity(T):
 @pytest.mark.parametrize("kw", [
     dict(k=0), dict(k=2049), dict(max_rows=0), dict(max_len=-1), dict(max_len=1 << 31),
     dict(force_path=4), dict(force_path=-1), dict(wg_per_row=1), dict(wg_per_row=-2),
-    dict(cand_capacity=-1), dict(min_chunk=-5),
+    dict(cand_capacity=-1), dict(min_chunk=-5), dict(spin_limit=-2),
 ])
 def test_bad_config_rejected_without_gpu(T, kw):
     base = dict(k=2048, max_rows=7, max_len=80_000)
@@ -92,6 +92,8 @@ def test_null_arguments_rejected(T):
     assert lib.topk_debug_stream_read(None, 8, None, None, None, None) == T.TOPK_ERR_INVALID_ARG
     assert lib.topk_debug_stream_read(None, -1, None, None, None, None) == T.TOPK_ERR_INVALID_ARG
     assert lib.topk_stream_read_groups() >= 1
+    assert lib.topk_debug_histogram(None, 0, None, 3, 2048, None, None, None) == T.TOPK_ERR_INVALID_ARG
+    assert lib.topk_debug_histogram(None, 0, None, 0, 0, None, None, None) == T.TOPK_ERR_INVALID_ARG
     bad = T.make_config(0, 7, 80_000)
     assert lib.topk_plan(ctypes.byref(bad), None, 7, None, 0, None) == T.TOPK_ERR_INVALID_ARG
     assert lib.topk_select_paged(ctypes.byref(bad), None, None, 0, None, 7, None, 0, 64,
@@ -110,3 +112,20 @@ def test_valid_config_needs_a_device(T):
     with pytest.raises(T.TopKError) as e:
         T.topk_query_sizes(T.make_config(2048, 7, 80_000))
     assert e.value.status == T.TOPK_ERR_HIP
+
+
+def test_binding_rejects_strided_lengths_and_tables(T):
+    """A strided view of the lengths or a block table without unit page
+    stride would be read as other data by the library: the binding refuses
+    both before any device call."""
+    import torch
+    lengths = torch.arange(14, dtype=torch.int32)[::2]
+    table = torch.zeros((4, 8), dtype=torch.int32).t()
+    ok_table = torch.zeros((4, 8), dtype=torch.int32)
+    cfg = T.make_config(2048, 7, 80_000)
+    with pytest.raises(ValueError, match="lengths"):
+        T.topk_plan(cfg, lengths, torch.zeros(16, dtype=torch.int32))
+    with pytest.raises(ValueError, match="lengths"):
+        T._select_args(cfg, None, None, lengths, ok_table, 0, 64, None, None, None, None)
+    with pytest.raises(ValueError, match="block_table"):
+        T._select_args(cfg, None, None, lengths.contiguous(), table, 8, 64, None, None, None, None)

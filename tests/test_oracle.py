@@ -230,6 +230,80 @@ def test_canonical_sorts_by_position(oracle_mod):
     assert ci.tolist() == [[2, 5, 9, -1, -1]] and cs.tolist() == [[20, 50, 90, -1, -1]]
 
 
+# Hand-worked rows for the two comparators: each row is reordered on its own,
+# slots travel with their positions, and -1 padding stays at the end. Row 1's
+# slots are not ordered like its positions (the table is a permutation), so a
+# comparator that sorted slots by slot value, or sorted across rows, or moved
+# -1 to the front, gives a different answer.
+_CANON_IDX = np.array([[7, 0, 3, -1, -1],
+                       [1, 9, 4, 2, -1],
+                       [-1, -1, -1, -1, -1]], np.int32)
+_CANON_SLOTS = np.array([[455, 128, 195, -1, -1],
+                         [65, 9, 388, 130, -1],
+                         [-1, -1, -1, -1, -1]], np.int32)
+_CANON_WANT_IDX = [[0, 3, 7, -1, -1], [1, 2, 4, 9, -1], [-1, -1, -1, -1, -1]]
+_CANON_WANT_SLOTS = [[128, 195, 455, -1, -1], [65, 130, 388, 9, -1], [-1, -1, -1, -1, -1]]
+# slot-only comparison: each row's slots ascending, -1 (as the int64 maximum) last
+_BIG = int(np.iinfo(np.int64).max)
+_CANON_WANT_SLOT_ONLY = [[128, 195, 455, _BIG, _BIG], [9, 65, 130, 388, _BIG], [_BIG] * 5]
+
+
+def _canonical_pins_pass(canonical, canonical_slots) -> bool:
+    ci, cs = canonical(_CANON_IDX, _CANON_SLOTS)
+    if np.asarray(ci).tolist() != _CANON_WANT_IDX or np.asarray(cs).tolist() != _CANON_WANT_SLOTS:
+        return False
+    return np.asarray(canonical_slots(_CANON_SLOTS)).tolist() == _CANON_WANT_SLOT_ONLY
+
+
+def test_canonical_multi_row_hand_worked(oracle_mod):
+    assert _canonical_pins_pass(oracle_mod.canonical, oracle_mod.canonical_slots)
+
+
+def test_canonical_slots_keeps_rows_apart(oracle_mod):
+    """Two outputs of the same row set in different orders compare equal; a
+    slot moved to another row does not."""
+    a = np.array([[3, 1, 2, -1], [8, 6, -1, -1]], np.int32)
+    b = np.array([[2, 3, 1, -1], [-1, 6, 8, -1]], np.int32)
+    c = np.array([[3, 1, 8, -1], [2, 6, -1, -1]], np.int32)
+    sa, sb, sc = (oracle_mod.canonical_slots(x) for x in (a, b, c))
+    assert np.array_equal(sa, sb)
+    assert not np.array_equal(sa, sc)
+
+
+def _canon_slots_axis0(slots):
+    s = np.asarray(slots).astype(np.int64)
+    return np.sort(np.where(s < 0, np.iinfo(np.int64).max, s), axis=0)
+
+
+def _canon_slots_minus_one_first(slots):
+    return np.sort(np.asarray(slots).astype(np.int64), axis=1)
+
+
+def _canon_by_slot(idx, slots):
+    order = np.argsort(np.where(np.asarray(slots) < 0, np.iinfo(np.int64).max, slots), axis=1, kind="stable")
+    return np.take_along_axis(idx, order, axis=1), np.take_along_axis(slots, order, axis=1)
+
+
+def _canon_slots_unmoved(idx, slots):
+    key = np.where(idx < 0, np.iinfo(np.int64).max, idx.astype(np.int64))
+    return np.sort(key, axis=1).astype(np.int32), np.asarray(slots)
+
+
+@pytest.mark.parametrize("mistake", ["slots_axis0", "slots_minus_one_first", "canon_by_slot",
+                                     "canon_slots_unmoved"])
+def test_canonical_planted_mistakes(oracle_mod, mistake):
+    canonical, canonical_slots = oracle_mod.canonical, oracle_mod.canonical_slots
+    if mistake == "slots_axis0":
+        canonical_slots = _canon_slots_axis0
+    elif mistake == "slots_minus_one_first":
+        canonical_slots = _canon_slots_minus_one_first
+    elif mistake == "canon_by_slot":
+        canonical = _canon_by_slot
+    else:
+        canonical = _canon_slots_unmoved
+    assert not _canonical_pins_pass(canonical, canonical_slots)
+
+
 # --- planted mistakes: each mutated copy of the oracle must fail a pin --------
 
 MUTATIONS = {

@@ -345,3 +345,181 @@ def test_plan_and_select_replay_from_a_hip_graph(rows, max_len):
         _gpu.say(f"[graph] rows {rows} replay {rep}")
         _gpu.assert_matches_oracle(w, (idx.cpu().numpy(), slots.cpu().numpy()), f"graph replay {rep}")
     assert tk.status() == 0
+
+
+@pytest.fixture(scope="module")
+def plan_split():
+    return synth.make_plan_split()
+
+
+def _plan_header_items(tk):
+    """(num_items, num_multi_items, num_groups) from the plan the planning
+    kernel wrote (64-byte header: magic, rows, items, split items, grid, k,
+    groups, ...)."""
+    h = tk.plan_buf[:16].cpu().numpy()
+    assert h[0] == 0x31504B54, "the planning kernel wrote no plan"
+    return int(h[2]), int(h[3]), int(h[6])
+
+
+@pytest.mark.parametrize("kw", [{}, {"min_chunk": 8192}], ids=["default", "min_chunk8192"])
+def test_plan_kernel_emits_split_rows(plan_split, kw):
+    """600 rows, four of 300,000 positions: more rows than the selection
+    kernel plans itself, so topk_plan's kernel writes the work list, and the
+    long rows are split across workgroups by it (its split-row branch)."""
+    from sparse_attention_indexer_amd import topk
+    w = plan_split
+    dev = torch.device("cuda:0")
+    _gpu.say(f"[plan split] 600 rows, 4 x 300,000, {kw}")
+    tk = topk.TopK(w.k, w.rows, w.max_len, device=dev, **kw)
+    sc = torch.from_numpy(w.scores).to(dev)
+    ln = torch.from_numpy(w.lengths).to(dev)
+    bt = torch.from_numpy(np.ascontiguousarray(w.block_table)).to(dev)
+    tk.plan(ln)
+    slots, idx = tk.select(sc, ln, bt, w.bt_row_stride, w.page_size)
+    torch.cuda.synchronize()
+    assert tk.status() == 0
+    n_items, n_multi, n_groups = _plan_header_items(tk)
+    _gpu.say(f"[plan split] items {n_items}, split items {n_multi}, split rows {n_groups}")
+    assert n_groups == 4 and n_multi >= 8 and n_items == n_multi + (w.rows - 4)
+    _gpu.assert_matches_oracle(w, (idx.cpu().numpy(), slots.cpu().numpy()), f"plan split {kw}")
+
+
+def test_plan_kernel_split_rows_replay_from_a_hip_graph():
+    """topk_plan (planning kernel, split rows) + topk_select_paged captured
+    into a HIP graph and replayed with two batches of different lengths copied
+    in eagerly before each replay; every replay must match the oracle."""
+    from sparse_attention_indexer_amd import topk
+    dev = torch.device("cuda:0")
+    cases = [synth.make_plan_split(seed=8 + i) for i in range(2)]
+    w0 = cases[0]
+    tk = topk.TopK(w0.k, w0.rows, w0.stride, device=dev)
+    sc = torch.from_numpy(w0.scores).to(dev)
+    ln = torch.from_numpy(w0.lengths).to(dev)
+    bt = torch.from_numpy(np.ascontiguousarray(w0.block_table)).to(dev)
+    slots = torch.empty((w0.rows, w0.k), dtype=torch.int32, device=dev)
+    idx = torch.empty_like(slots)
+    tk.plan(ln)
+    tk.select(sc, ln, bt, w0.bt_row_stride, w0.page_size, out_slots=slots, out_indices=idx)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        tk.plan(ln)
+        tk.select(sc, ln, bt, w0.bt_row_stride, w0.page_size, out_slots=slots, out_indices=idx)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        w = cases[rep % 2]
+        sc.copy_(torch.from_numpy(w.scores))
+        ln.copy_(torch.from_numpy(w.lengths))
+        bt.copy_(torch.from_numpy(np.ascontiguousarray(w.block_table)))
+        slots.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _gpu.say(f"[graph plan split] replay {rep}")
+        _gpu.assert_matches_oracle(w, (idx.cpu().numpy(), slots.cpu().numpy()), f"split graph replay {rep}")
+    assert tk.status() == 0
+
+
+def test_split_row_wait_gives_up_and_workspace_recovers():
+    """The split-row wait's time-out path, forced from the host: with
+    spin_limit -1 every workgroup of a split row gives up before its first
+    poll. The kernel must end, report TOPK_DEVICE_SPIN_TIMEOUT, and after
+    topk_workspace_init the same workspace must give the oracle's result."""
+    from sparse_attention_indexer_amd import topk
+    w = synth.random_case(61, rows=7, max_len=100_000, alphabet=0, k=2048, exact_len=True)
+    dev = torch.device("cuda:0")
+    tk = topk.TopK(w.k, w.rows, w.max_len, device=dev, spin_limit=-1)
+    sc = torch.from_numpy(np.ascontiguousarray(w.scores)).to(dev)
+    ln = torch.from_numpy(w.lengths).to(dev)
+    bt = torch.from_numpy(np.ascontiguousarray(w.block_table)).to(dev)
+    _gpu.say("[timeout] 7 x 100,000 split rows, spin_limit -1")
+    tk.plan(ln)
+    tk.select(sc, ln, bt, w.bt_row_stride, w.page_size)
+    torch.cuda.synchronize()   # the kernel ended
+    st = tk.status()
+    assert st & topk.DEVICE_SPIN_TIMEOUT, f"status {st}: the forced time-out was not reported"
+    assert st & ~topk.DEVICE_SPIN_TIMEOUT == 0, f"status {st}"
+    # one poll at most: either every row's merge was complete at its first
+    # poll or the time-out is reported; the kernel ends either way
+    tk.cfg.spin_limit = 1
+    topk.topk_workspace_init(tk.workspace)
+    tk.select(sc, ln, bt, w.bt_row_stride, w.page_size)
+    torch.cuda.synchronize()
+    st = tk.status()
+    assert st in (0, topk.DEVICE_SPIN_TIMEOUT), f"status {st}"
+    _gpu.say(f"[timeout] spin_limit 1 -> status {st}")
+    tk.cfg.spin_limit = 0
+    topk.topk_workspace_init(tk.workspace)
+    for rep in range(2):
+        got = tk.select(sc, ln, bt, w.bt_row_stride, w.page_size)
+        torch.cuda.synchronize()
+        assert tk.status() == 0
+        _gpu.assert_matches_oracle(w, (got[1].cpu().numpy(), got[0].cpu().numpy()), f"after re-init {rep}")
+
+
+def test_prefill_4096_rows_full_size():
+    """Ragged prefill top-k at full size: 4,096 causal rows of 80,000 + t
+    positions (the planning kernel's regime), bit-exact against the oracle."""
+    w = synth.make_prefill()
+    _gpu.say(f"[prefill] {w.rows} rows x up to {w.max_len}")
+    got = _gpu.run_gpu(w, "auto")
+    _gpu.assert_matches_oracle(w, got, "prefill 4096x80k")
+
+
+def _key16_bins(x: np.ndarray) -> np.ndarray:
+    """Ordered 1,024-bin index of each score: numpy's FP16 rounding (RNE),
+    -0 folded into +0, sign-magnitude bits flipped into unsigned order, top
+    10 bits (the Figure 3 caption's key), written out here from the
+    definition, independently of the kernel."""
+    h = x.astype(np.float16)
+    h[h == 0] = np.float16(0.0)
+    hb = h.view(np.uint16).astype(np.uint32)
+    key = np.where(hb & 0x8000, (~hb) & 0xFFFF, hb | 0x8000)
+    return key >> 6
+
+
+@pytest.mark.parametrize("case", ["c1", "c2", "c3", "c5_rows", "fuzz_special", "short_rows"])
+def test_device_histogram_and_threshold_bin(workloads, case):
+    """The kernel's coarse histogram equals a CPU histogram of the same keys
+    (exact counts, summing to the row length), and its threshold bin is the
+    bin of the oracle's k-th score, with above(b*) < k <= above(b*) + h[b*]."""
+    from sparse_attention_indexer_amd import topk
+    if case.startswith("c") and case != "c5_rows":
+        w = workloads[int(case[1])]
+    elif case == "c5_rows":
+        w = c5_half(workloads[5])
+    elif case == "fuzz_special":
+        w = synth.random_case(505, rows=9, max_len=70_000, alphabet=0, special=True, k=1500)
+    else:
+        w = synth.random_case(506, rows=6, max_len=3000, alphabet=7, special=True, k=2048)
+    _gpu.say(f"[hist] {case}: {w.rows} x {w.stride}")
+    dev = torch.device("cuda:0")
+    hist, thr = topk.topk_debug_histogram(torch.from_numpy(np.ascontiguousarray(w.scores)).to(dev),
+                                          torch.from_numpy(w.lengths).to(dev), w.k)
+    hist = hist.cpu().numpy().view(np.uint32).astype(np.int64)
+    thr = thr.cpu().numpy().view(np.uint32).astype(np.int64)
+    ref_idx, _ = oracle_sorted(w)
+    # Ordered bins 15 (-inf) .. 1008 (+inf) hold every non-NaN score; the
+    # others hold only NaN codes. The kernel counts a tile's NaN padding past
+    # the row's end there and never scans them.
+    lo, hi = 15, 1009
+    for r in range(w.rows):
+        n = int(w.lengths[r])
+        want = np.bincount(_key16_bins(w.scores[r, :n]), minlength=1024)
+        assert want[:lo].sum() == 0 and want[hi:].sum() == 0
+        np.testing.assert_array_equal(hist[r, lo:hi], want[lo:hi], err_msg=f"{case} row {r}")
+        assert hist[r, lo:hi].sum() == n
+        if n <= w.k:
+            assert thr[r, 0] == 0xFFFFFFFF
+            continue
+        b, above, cnt = thr[r]
+        vk = w.scores[r, ref_idx[r, w.k - 1]]
+        assert b == _key16_bins(np.array([vk], np.float32))[0], f"{case} row {r}"
+        assert above == hist[r, b + 1:].sum() and cnt == hist[r, b]
+        assert above < w.k <= above + cnt
+
+
+def oracle_sorted(w):
+    """The oracle's output in its own (score desc, position asc) order."""
+    import oracle
+    return oracle.topk_workload(w, threads=8)
