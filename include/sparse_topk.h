@@ -201,6 +201,32 @@ enum {
 topk_status topk_read_status(const void* workspace, size_t workspace_bytes,
                              int32_t* host_status, void* stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * selection as topk_select_paged, with no plan buffer and no workspace
+ * argument. The cross-workgroup state lives in a library-owned device array of
+ * TOPK_NOALLOC_SCRATCH_BYTES per GPU (held until the process ends). The
+ * call allocates nothing. It enqueues a fill kernel that clears the part of
+ * that array the call uses, then the selection kernel.
+ *   Arguments as for topk_select_paged. The batch must be planned inside the
+ *   selection kernel: num_rows <= TOPK_IN_KERNEL_PLAN_ROWS, else UNSUPPORTED.
+ *   The workspace topk_query_sizes reports for cfg must fit the array, else
+ *   BUFFER_TOO_SMALL (nothing enqueued).
+ *   device_status   int32 (device) or NULL: when given, the kernel ORs its
+ *                   TOPK_DEVICE_* flags into it (the caller zeroes it first);
+ *                   when NULL, they are not reported.
+ * Every call on one GPU shares that GPU's array: calls that can overlap on one
+ * GPU (two streams, two threads) race and give undefined results. Status: OK,
+ * INVALID_ARG, BUFFER_TOO_SMALL, UNSUPPORTED, HIP. No host synchronisation.
+ */
+#define TOPK_NOALLOC_SCRATCH_BYTES (16u << 20)
+topk_status topk_select_paged_noalloc(const topk_config* cfg, const float* scores, int64_t score_row_stride,
+                                      const int32_t* lengths, int32_t num_rows, const int32_t* block_table,
+                                      int64_t bt_row_stride, int32_t page_size, int32_t* out_slots,
+                                      int32_t* out_indices, int64_t out_row_stride, int32_t* device_status,
+                                      void* stream);
+
 /* Elements one workgroup holds in registers (the register path's row limit).
  * Passage: TopK-V2 text, the register-resident path for short rows; the
  * limit itself is this library's tile size. */

@@ -194,7 +194,7 @@ topk_status select_impl(const topk_config* cfg, const void* plan, const float* s
                         const int32_t* lengths, int32_t num_rows, const int32_t* block_table, int64_t bt_row_stride,
                         int32_t page_size, int32_t* out_slots, int32_t* out_indices, int64_t out_row_stride,
                         void* workspace, size_t workspace_bytes, void* stream, void* start_event,
-                        void* stop_event) {
+                        void* stop_event, int32_t* device_status = nullptr) {
   Sizing s;
   const topk_status st = sizing(cfg, &s);
   if (st != TOPK_OK) return st;
@@ -232,7 +232,7 @@ topk_status select_impl(const topk_config* cfg, const void* plan, const float* s
   a.groups = (GroupState*)((char*)workspace + ws_group_offset());
   a.cand = (uint64_t*)((char*)workspace + ws_cand_offset(s));
   a.cand_cap = s.cand_cap;
-  a.status = (int32_t*)workspace;
+  a.status = device_status ? device_status : (int32_t*)workspace;
   a.max_len = cfg->max_len;
   a.spin_limit = cfg->spin_limit == 0 ? kDefaultSpinLimit : cfg->spin_limit < 0 ? 0u : (uint32_t)cfg->spin_limit;
   // The selection kernel starts loading its tile before the lengths arrive,
@@ -308,6 +308,70 @@ topk_status topk_read_status(const void* workspace, size_t workspace_bytes, int3
 
 int64_t topk_register_capacity(void) { return kTile; }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The library-owned workspace of topk_select_paged_noalloc: one array per
+// device (each GPU holds its own copy for the life of the process). Host code
+// never uses the array's name as an address; it uses the per-device pointer
+// from hipGetSymbolAddress.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;   // TOPK_NOALLOC_SCRATCH_BYTES
+static_assert(kNoAllocScratchBytes == TOPK_NOALLOC_SCRATCH_BYTES, "header and library agree");
+
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+void* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The calling thread's current device's copy of `scratch`, looked up once per
+// device (with that device current).
+topk_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TOPK_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TOPK_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TOPK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+topk_status topk_select_paged_noalloc(const topk_config* cfg, const float* scores, int64_t score_row_stride,
+                                      const int32_t* lengths, int32_t num_rows, const int32_t* block_table,
+                                      int64_t bt_row_stride, int32_t page_size, int32_t* out_slots,
+                                      int32_t* out_indices, int64_t out_row_stride, int32_t* device_status,
+                                      void* stream) {
+  Sizing s;
+  topk_status st = sizing(cfg, &s);
+  if (st != TOPK_OK) return st;
+  if (!select_args_ok(cfg, score_row_stride, num_rows, scores, lengths, block_table, bt_row_stride, page_size,
+                      out_slots, out_row_stride))
+    return TOPK_ERR_INVALID_ARG;
+  if (num_rows > kInKernelPlanRows || s.grid >= 4096) return TOPK_ERR_UNSUPPORTED;   // needs a plan buffer
+  if (s.workspace_bytes > kNoAllocScratchBytes) return TOPK_ERR_BUFFER_TOO_SMALL;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != TOPK_OK) return st;
+  // Clear what must start at zero on every call (the status word and the
+  // split rows' group states; candidate slabs are written before they are
+  // read): a previous call may have left them dirty by timing out, and every
+  // call on this device shares them. A fill kernel, not a memset node.
+  if (num_rows == 0) return TOPK_OK;
+  const size_t clear = ws_cand_offset(s);
+  if (launch_fill(ws, clear, (hipStream_t)stream) != hipSuccess) return TOPK_ERR_HIP;
+  return select_impl(cfg, nullptr, scores, score_row_stride, lengths, num_rows, block_table, bt_row_stride,
+                     page_size, out_slots, out_indices, out_row_stride, ws, s.workspace_bytes, stream, nullptr,
+                     nullptr, device_status);
+}
 
 topk_status topk_debug_keys(const float* x, int64_t n, uint32_t* bin_out, uint32_t* key32_out, void* stream) {
   if (n < 0 || (n > 0 && !x)) return TOPK_ERR_INVALID_ARG;

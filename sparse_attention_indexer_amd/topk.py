@@ -65,6 +65,7 @@ def load_library():
         "topk_debug_keys": [V, I64, V, V, V],
         "topk_debug_stream_read": [V, I64, V, V, V, V],
         "topk_debug_histogram": [V, I64, V, I32, I32, V, V, V],
+        "topk_select_paged_noalloc": [P, V, I64, V, I32, V, I64, I32, V, V, I64, V, V],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
@@ -172,6 +173,21 @@ def topk_select_paged(cfg: topk_config, plan: torch.Tensor, scores: torch.Tensor
     args = _select_args(cfg, plan, scores, lengths, block_table, bt_row_stride, page_size, out_slots,
                         out_indices, workspace, stream)
     _check("topk_select_paged", load_library().topk_select_paged(*args))
+
+
+def topk_select_paged_noalloc(cfg: topk_config, scores: torch.Tensor, lengths: torch.Tensor,
+                              block_table: torch.Tensor, bt_row_stride: int, page_size: int,
+                              out_slots: torch.Tensor, out_indices: torch.Tensor | None,
+                              device_status: torch.Tensor | None = None, stream=None) -> None:
+    """topk_select_paged with no plan or workspace: the library's own device
+    array holds the cross-workgroup state (batches planned in the kernel)."""
+    args = _select_args(cfg, None, scores, lengths, block_table, bt_row_stride, page_size, out_slots,
+                        out_indices, None, stream)
+    if device_status is not None:
+        _need(device_status, torch.int32, "device_status")
+    # (cfg, scores, stride, lengths, rows, table, bt stride, page size, slots, indices, out stride)
+    _check("topk_select_paged_noalloc", load_library().topk_select_paged_noalloc(
+        *args[0:1], *args[2:12], _ptr(device_status), args[14]))
 
 
 def _event_handle(ev: "torch.cuda.Event") -> int:

@@ -67,6 +67,15 @@ int main() {
     CHECK(topk_select_paged(&x, nullptr, nullptr, 0, nullptr, 1, nullptr, 0, 64, nullptr, nullptr, 2048, nullptr, 0,
                             nullptr) == TOPK_ERR_INVALID_ARG,
           b.what);
+    CHECK(topk_select_paged_noalloc(&x, nullptr, 0, nullptr, 1, nullptr, 0, 64, nullptr, nullptr, 2048, nullptr,
+                                    nullptr) == TOPK_ERR_INVALID_ARG,
+          b.what);
+  }
+  {
+    topk_config x = good();
+    const topk_status n = topk_select_paged_noalloc(&x, nullptr, 80000, nullptr, 7, nullptr, 0, 64, nullptr, nullptr,
+                                                    2048, nullptr, nullptr);
+    CHECK(n == TOPK_ERR_HIP || n == TOPK_ERR_INVALID_ARG, "no-alloc call with NULL buffers");
   }
   topk_config reg = good();
   reg.force_path = TOPK_PATH_REGISTER;
