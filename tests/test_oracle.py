@@ -13,6 +13,7 @@ import ctypes
 import itertools
 import os
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -328,7 +329,7 @@ def _build_mutant(tmp_path, name, old, new):
     path.write_text(src.replace(old, new))
     so = tmp_path / f"{name}.so"
     subprocess.check_call(["gcc", "-O1", "-fPIC", "-shared", "-o", str(so), str(path), "-lm"])
-    return ctypes.CDLL(str(so))
+    return str(so)
 
 
 class _MutantOracle:
@@ -391,8 +392,24 @@ def test_pins_accept_real_oracle(oracle_mod):
     assert _pins_pass(oracle_mod)
 
 
+# Run in a child process: several mutants read or write out of bounds (a
+# padding rule dropped reads past the sorted pairs, a length ignored overruns
+# the pair buffer), and the resulting crash must not take the test run down.
+# Exit status 0 means the pins accepted the mutant; 3 that they rejected it;
+# a crash also counts as rejected, since the pins could not pass.
+_CHILD = """
+import ctypes, sys
+sys.path.insert(0, sys.argv[1])
+from tests import test_oracle as t
+mutant = t._MutantOracle(ctypes.CDLL(sys.argv[2]))
+sys.exit(0 if t._pins_pass(mutant) else 3)
+"""
+
+
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_planted_mistakes(tmp_path, name):
     old, new = MUTATIONS[name]
-    mutant = _MutantOracle(_build_mutant(tmp_path, name, old, new))
-    assert not _pins_pass(mutant), f"pins did not catch mutation {name}"
+    so = _build_mutant(tmp_path, name, old, new)
+    p = subprocess.run([sys.executable, "-c", _CHILD, ROOT, so], capture_output=True, text=True, timeout=300)
+    assert p.returncode != 0, f"pins did not catch mutation {name}"
+    assert p.returncode == 3 or p.returncode < 0, p.stderr[-2000:]
