@@ -99,7 +99,9 @@ topk_status sizing(const topk_config* cfg, Sizing* s) {
   s->max_groups = groups;
   const int64_t cand = cfg->cand_capacity > 0 ? cfg->cand_capacity
                                              : (cfg->max_len < kDefaultCandCap ? cfg->max_len : kDefaultCandCap);
-  s->cand_cap = cand < 1 ? 1 : cand;
+  // even, so that every row's candidate slab starts on a 16-byte boundary
+  // (the slabs are copied to LDS 16 bytes per lane)
+  s->cand_cap = cand < 2 ? 2 : (cand + 1) / 2 * 2;
   const bool splits = cfg->force_path == TOPK_PATH_AUTO || cfg->force_path == TOPK_PATH_MULTI;
   // every row split needs its own group state and at least two workgroups of one grid round
   if (cfg->force_path == TOPK_PATH_MULTI && (int64_t)cfg->max_rows * 2 > s->grid) return TOPK_ERR_UNSUPPORTED;

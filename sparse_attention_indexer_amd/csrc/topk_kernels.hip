@@ -243,7 +243,6 @@ constexpr int kFirstRadixBins = 1 << kFirstRadixBits;
 constexpr int kWidePad = 4;                         // one pad word per 16 bins: conflict-free threshold scan
 constexpr int kWideWords = kFirstRadixBins + (kFirstRadixBins >> kWidePad);
 constexpr int kWideSlots = kWideWords / 2;          // list entries the padded histogram occupies
-constexpr int kLoadBatch = 24;                      // candidates per lane in flight when the resolver fills LDS
 constexpr int kResolveRegs = 24;                    // candidates per lane of the register-resident first pass
 // While a split row's workgroup waits for the others it re-reads the scores
 // that will probably be needed: those in bins at or above the one holding
@@ -255,6 +254,10 @@ constexpr int kResolveRegs = 24;                    // candidates per lane of th
 constexpr int kPreRegs = 4;
 constexpr int kPreCap = kPreRegs * kBlock;
 constexpr int kStageCap = kListCap - kPreCap / 2;  // staged candidates below the position list
+// A split row's per-workgroup fine-digit counters (32 KB) sit in the LDS list
+// above at most kFineListOff staged candidates and below the position list.
+constexpr int kFineListOff = 8192;
+static_assert(kFineListOff + kFineBins / 2 <= kStageCap, "fine-digit counters below the position list");
 static_assert(kWideWords * 4 <= kListCap * 8, "first-digit histogram aliases the LDS list");
 static_assert(kMaxK <= kRadixBins, "above-threshold staging aliases rhist");
 
@@ -784,6 +787,47 @@ __device__ __forceinline__ Refine make_refine(const uint32_t* range, uint32_t ne
   return p;
 }
 
+// FP32-key digit of a threshold-bin candidate in a frame that depends on the
+// bin alone, so every workgroup of a split row computes the same digit
+// without another exchange. A score whose FP16 rounding lies in ordered bin
+// b lies strictly between the FP16 values just below and just above the bin
+// (rounding is monotone and both are exactly representable in FP32), so its
+// key32 lies in [lo, hi] with lo, hi the keys of those two values (the key of
+// -0 is the key of +0, hence not strictly). Beyond -inf or +inf (NaN codes)
+// the frame runs to the end of the key range. The digit is the key offset
+// from lo shifted right until the frame fits 13 bits, clamped: a monotone
+// function of the key, so a digit above another means a larger score.
+struct FineFrame {
+  uint32_t lo;
+  uint32_t shift;
+  __device__ __forceinline__ uint32_t digit(uint32_t key) const {
+    const uint32_t d = key >= lo ? (key - lo) >> shift : 0u;
+    return min(d, (uint32_t)kFineBins - 1u);
+  }
+};
+__device__ __forceinline__ bool key16_is_nan(uint32_t key16) {
+  const uint32_t h = half_bits_of_key16(key16);
+  return (h & 0x7C00u) == 0x7C00u && (h & 0x03FFu) != 0u;
+}
+__device__ __forceinline__ uint32_t key32_of_key16(uint32_t key16) {
+  return key32_of((float)half_of_bits(half_bits_of_key16(key16)));
+}
+// b is a threshold bin, so kFirstBin <= b <= kLastBin: both neighbours are
+// 16-bit codes.
+__device__ __forceinline__ FineFrame fine_frame(uint32_t b) {
+  const uint32_t below = b * 64u - 1u, above = b * 64u + 64u;
+  FineFrame f;
+  f.lo = key16_is_nan(below) ? 0u : key32_of_key16(below);
+  const uint32_t hi = key16_is_nan(above) ? 0xFFFFFFFFu : key32_of_key16(above);
+  const uint32_t w = bit_width(hi - f.lo);
+  f.shift = w > (uint32_t)kFineBits ? w - (uint32_t)kFineBits : 0u;
+  return f;
+}
+// Split rows whose threshold bin holds more candidates than this count them
+// by fine digit as they classify (below it the last workgroup's register pass
+// is cheap), up to what that pass holds in registers.
+constexpr uint32_t kFineMin = 4096;
+
 // --- candidate sources for the exact refinement -----------------------------
 // each(f) calls f(valid, composite key) for every element slot; the trip count
 // is uniform across the workgroup so wave-level ballots stay convergent.
@@ -1093,15 +1137,17 @@ __device__ __forceinline__ void pairs_to_keys(Smem& sh, uint32_t n, const Refine
   __syncthreads();
 }
 
-// The pair list sh.list[0, n) (n <= J * kBlock) into registers, then the
-// register-resident first pass.
+// The pair list src[0, n) in LDS (default sh.list; n <= J * kBlock) into
+// registers, then the register-resident first pass.
 template <int J>
-__device__ __forceinline__ void resolve_lds_pairs(uint32_t n, const Refine& p, Smem& sh, const RowOut& o) {
+__device__ __forceinline__ void resolve_lds_pairs(uint32_t n, const Refine& p, Smem& sh, const RowOut& o,
+                                                  const uint64_t* src = nullptr) {
+  if (!src) src = sh.list;
   uint32_t kd[J], ps[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const uint32_t i = (uint32_t)j * kBlock + threadIdx.x;
-    const uint64_t v = i < n ? sh.list[i] : 0ull;
+    const uint64_t v = i < n ? src[i] : 0ull;
     kd[j] = (uint32_t)(v >> 32) - p.lo32;
     ps[j] = (uint32_t)v;
   }
@@ -1218,44 +1264,284 @@ __device__ __forceinline__ void resolve_global_regs(const GroupState* g, const u
   resolve_regs<J, true>(kd, ps, n, p, sh, o);
 }
 
+// Whole workgroup: copy n 64-bit words that other workgroups wrote (agent
+// scope) from src to LDS dst with direct-to-LDS loads (global_load_lds, 16
+// bytes per lane, cache policy sc1 = device coherent), so the data in flight
+// holds no registers. Each wave instruction moves 128 consecutive words; lanes
+// past n re-read the last word (in bounds) into slots past n, so dst must have
+// room for n rounded up to 128. The caller waits (vmcnt) and synchronises.
+constexpr int kLdsCopyWords = kWave * 2;   // 64-bit words per wave instruction
+__device__ __forceinline__ void copy_agent_to_lds(const uint64_t* src, uint32_t n, uint64_t* dst) {
+  if (n == 0) return;
+  const uint32_t w = uni(threadIdx.x >> 6);
+  for (uint32_t base = w * kLdsCopyWords; base < n; base += kWaves * kLdsCopyWords) {
+    const uint32_t i = min(base + 2u * lane(), (n - 1u) & ~1u);   // even, so the 16-byte load stays aligned
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + i),
+                                     (__attribute__((address_space(3))) void*)(dst + base), 16, 0, 16);
+  }
+}
+
+// A fine row's last workgroup copies up to kFineMaxCand candidates to the LDS
+// list, then the digit counts above them.
+constexpr uint32_t kFineMaxCand = kResolveRegs * kBlock;      // 12,288 candidates ...
+constexpr uint32_t kFineHistEntry = kFineMaxCand;             // ... then the digit counts
+static_assert(kFineHistEntry + kFineBins / 2 <= (uint32_t)kListCap, "candidates and digit counts share the LDS list");
+static_assert(kFineMaxCand % kLdsCopyWords == 0, "the rounded-up copy stays below the digit counts");
+
+// The composite key of a threshold-bin candidate of a split row in its fine
+// digit's frame: ((key32 - lo) << b2) | (len - 1 - position), with
+// b2 = bitwidth(len - 1) and 13 + shift key bits (every candidate's key
+// offset is below 2^(13 + shift)), so its top 13 bits are its fine digit.
+// Every workgroup of the row derives it from the threshold bin and the row
+// length alone; the producers store candidates in this form.
+__device__ __forceinline__ Refine fine_key_frame(FineFrame fr, uint32_t len) {
+  Refine p;
+  p.lo32 = fr.lo;
+  p.idx_hi = len - 1u;
+  p.b2 = bit_width(len - 1u);
+  p.nb = (uint32_t)kFineBits + fr.shift + p.b2;
+  p.need = 0;
+  p.cnt = 0;
+  return p;
+}
+
+// Every workgroup of a split row whose threshold bin holds more than
+// kFineMin candidates ("fine" rows), after classifying its chunk: its
+// candidates sit in the LDS list as fine-frame composite keys (fine_key_frame)
+// and its fine-digit counts in LDS (fine_lds) or already in the row's digit
+// histogram. It adds its nonzero counts to the row's histogram (one atomic
+// each; a few hundred per workgroup), then reads that histogram until the
+// counts sum to the threshold bin's total: every
+// contribution only adds, so a read that reaches the total has read every
+// final count (the snapshot argument of the first wait). A scan from the top
+// finds the digit d* holding the need-th largest candidate. Each workgroup
+// then selects its own candidates above d* (all of d* when every candidate
+// there is needed) and sends only those in d* to the row's list; the last
+// workgroup resolves those few exactly and flushes the rest of the outputs.
+template <bool VEC>
+__device__ __forceinline__ void fine_tail(const SelectArgs& a, GroupState* g, uint64_t* slab, int32_t len,
+                                          uint32_t G, uint32_t k, uint32_t n_above, uint32_t cnt,
+                                          uint32_t local_above, bool fine_lds, Refine p, Smem& sh,
+                                          const RowOut& o, bool bad) {
+  const int t = threadIdx.x;
+  const uint32_t w = uni((uint32_t)t >> 6);
+  const uint32_t need = k - n_above;
+  const uint32_t* lfine = reinterpret_cast<const uint32_t*>(sh.list + kFineListOff);
+  __syncthreads();   // classification complete (staged list, digit counts, above-threshold outputs)
+  if (fine_lds) {
+    for (int i = t; i < kFineBins; i += kBlock) {
+      const uint32_t c = lfine[i];
+      if (c) __hip_atomic_fetch_add(&g->fine[i], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  bool ok = false;
+  // Lane t holds digits 8191 - 16 t down to 8176 - 16 t (lanes in thread order
+  // cover the digits from the top down), read as 8 word pairs.
+  constexpr int kPer = kFineBins / kBlock;
+  static_assert(kPer == 16, "16 digits per lane");
+  const uint32_t top = (uint32_t)(kFineBins - kPer * t) - 1u;
+  const uint64_t* fp = reinterpret_cast<const uint64_t*>(g->fine) + (top - (kPer - 1)) / 2;
+  uint32_t hv[kPer];
+  uint32_t s = 0, cum = 0;
+  for (uint32_t spins = 0; spins < a.spin_limit; ++spins) {
+    uint64_t q[kPer / 2];
+#pragma unroll
+    for (int i = 0; i < kPer / 2; ++i) q[i] = ld_agent(fp + i);
+    s = 0;
+#pragma unroll
+    for (int i = 0; i < kPer / 2; ++i) {
+      hv[2 * i] = (uint32_t)q[i];
+      hv[2 * i + 1] = (uint32_t)(q[i] >> 32);
+      s += hv[2 * i] + hv[2 * i + 1];
+    }
+    uint32_t tot;
+    cum = block_exclusive_add(s, sh.scratch, &tot);   // candidates in the digits above this lane's
+    if (uni(tot) == cnt) {
+      ok = true;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (!ok) {
+    if (t == 0) atomicOr(a.status, TOPK_DEVICE_SPIN_TIMEOUT);
+    return;
+  }
+  if (t == 0) sh.res[0] = kNotFound;
+  __syncthreads();
+  if (cum < need && need <= cum + s) {
+    // (selects, one store: a store per digit would hold 16 value triples;
+    // the digit's index i among the lane's 16, not the digit itself: per-i
+    // digit values are loop-invariant and would be hoisted into registers)
+    uint32_t c = cum, fi = 0, fc = 0, fh = 0;
+#pragma unroll
+    for (int i = kPer - 1; i >= 0; --i) {   // from digit top down
+      const uint32_t h = hv[i];
+      const bool hit = c < need && need <= c + h;
+      fi = hit ? (uint32_t)i : fi;
+      fc = hit ? c : fc;
+      fh = hit ? h : fh;
+      c += h;
+    }
+    sh.res[0] = top - (uint32_t)(kPer - 1) + fi;
+    sh.res[1] = fc;
+    sh.res[2] = fh;
+  }
+  __syncthreads();
+  const uint32_t dstar = uni(sh.res[0]), above = uni(sh.res[1]), cnt_d = uni(sh.res[2]);
+  const bool found = dstar != kNotFound;
+  const bool all_of_d = found && cnt_d == need - above;
+  const uint32_t dsel = all_of_d ? dstar : dstar + 1u;
+  const uint32_t dshift = p.nb - (uint32_t)kFineBits;
+  // This workgroup's candidates, each wave a contiguous share: counted first
+  // (ballots), then one atomic per row cursor reserves the workgroup's
+  // outputs and survivors, and the second pass writes them.
+  const uint32_t n_c = found ? min(uni(sh.cur_list), (uint32_t)kStageCap) : 0u;
+  const uint32_t per = ((n_c + kWaves - 1) / kWaves + kWave - 1) / kWave * kWave;
+  const uint32_t lo = min(w * per, n_c), hi = min(lo + per, n_c);
+  uint32_t nsel = 0, nkeep = 0;   // (uniform)
+  for (uint32_t i0 = lo; i0 < hi; i0 += kWave) {
+    const uint32_t i = i0 + lane();
+    const uint64_t v = i < hi ? sh.list[i] : 0ull;
+    const uint32_t d = (uint32_t)(v >> dshift);
+    nsel += (uint32_t)__popcll(__ballot(i < hi && d >= dsel));
+    nkeep += (uint32_t)__popcll(__ballot(i < hi && !all_of_d && d == dstar));
+  }
+  if (lane() == 0) {
+    reinterpret_cast<uint32_t*>(sh.pl_red)[w] = nsel;
+    reinterpret_cast<uint32_t*>(sh.pl_red)[kWaves + w] = nkeep;
+  }
+  __syncthreads();
+  uint32_t bsel = 0, bkeep = 0, tsel = 0, tkeep = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    const uint32_t cs = reinterpret_cast<const uint32_t*>(sh.pl_red)[i];
+    const uint32_t ck = reinterpret_cast<const uint32_t*>(sh.pl_red)[kWaves + i];
+    bsel += (uint32_t)i < w ? cs : 0u;
+    bkeep += (uint32_t)i < w ? ck : 0u;
+    tsel += cs;
+    tkeep += ck;
+  }
+  const uint32_t n_above_loc = min(uni(sh.cur_out), (uint32_t)kMaxK);   // staged above-threshold outputs
+  if (t == 0) {
+    // (the opaque zero keeps the plain fetch-add form: see the early atomics)
+    const uint32_t z = opaque_zero();
+    uint32_t bo = 0, bc = 0;
+    if (local_above + tsel) bo = __hip_atomic_fetch_add(&g->emit + z, local_above + tsel, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tkeep) bc = __hip_atomic_fetch_add(&g->cand + z, tkeep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh.bcast[0] = bo;
+    sh.bcast[1] = bc;
+  }
+  // Selected candidates join the staged outputs (their table entries are
+  // read below); survivors are staged past the candidates, or, when they do
+  // not fit there, stored to the row's list once the reservation returns.
+  const uint32_t surv_off = (n_c + 1u) & ~1u;
+  const bool room = n_above_loc + tsel <= (uint32_t)kMaxK;
+  const bool stage_surv = surv_off + tkeep <= (uint32_t)kStageCap;
+  if (!stage_surv) __syncthreads();
+  const uint32_t bc_direct = stage_surv ? 0u : uni(sh.bcast[1]);
+  uint32_t* staged = sh.rhist;
+  uint32_t* staged_pg = sh.outpos;
+  if (room) {
+    uint32_t ao = n_above_loc + bsel, ko = bkeep;
+    for (uint32_t i0 = lo; i0 < hi; i0 += kWave) {
+      const uint32_t i = i0 + lane();
+      const uint64_t v = i < hi ? sh.list[i] : 0ull;
+      const uint32_t d = (uint32_t)(v >> dshift);
+      const bool sel = i < hi && d >= dsel, kp = i < hi && !all_of_d && d == dstar;
+      const uint64_t ms = __ballot(sel), mk = __ballot(kp);
+      if (sel) staged[ao + mbcnt(ms)] = (uint32_t)p.pos(v);
+      if (kp) {
+        const uint32_t j = ko + mbcnt(mk);
+        if (stage_surv) {
+          sh.list[surv_off + j] = v;
+        } else {
+          const bool fits = (int64_t)(bc_direct + j) < a.cand_cap;
+          if (fits) st_agent(slab + bc_direct + j, v);
+          bad |= !fits;
+        }
+      }
+      ao += (uint32_t)__popcll(ms);
+      ko += (uint32_t)__popcll(mk);
+    }
+  }
+  bad |= !room || (found && tkeep > cnt_d);
+  __syncthreads();
+  // Stores: the outputs (table entries of the selected candidates read now,
+  // in flight with the reservation's round trip) and the survivors.
+  const uint32_t n_out = room ? n_above_loc + tsel : n_above_loc;
+  const uint32_t bo = uni(sh.bcast[0]), bc = uni(sh.bcast[1]);
+  for (uint32_t i = t; i < n_out; i += kBlock) {
+    const int32_t e = (int32_t)staged[i];
+    const int32_t pg = i < n_above_loc ? (int32_t)staged_pg[i] : ((uint32_t)e < (uint32_t)len ? o.page(e) : 0);
+    bad |= !o.store_page(bo + i, e, pg);
+  }
+  if (room && stage_surv)
+    for (uint32_t i = t; i < tkeep; i += kBlock) {
+      const bool fits = (int64_t)(bc + i) < a.cand_cap;
+      if (fits) st_agent(slab + bc + i, sh.list[surv_off + i]);
+      bad |= !fits;
+    }
+  report_bad(bad, a.status);
+  drain_memory();
+  __syncthreads();
+  if (t == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(&g->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh.flag = prev == G - 1u;
+  }
+  __syncthreads();
+  if (!uni(sh.flag)) return;
+  // The last workgroup: d*'s survivors (cnt_d, all in the list now) resolved
+  // exactly below the 13 bits fixed to d*, then the row's state left zeroed.
+  if (found && !all_of_d) {
+    if (t == 0) sh.cur_out = n_above + above;
+    copy_agent_to_lds(slab, cnt_d, sh.list);
+    drain_memory();
+    __syncthreads();
+    p.need = need - above;
+    p.cnt = cnt_d;
+    refine<true>(KeyListSrc{sh.list, cnt_d}, p, sh, o, (uint64_t)dstar, (uint32_t)kFineBits, need - above, cnt_d);
+    report_bad(!o.flush(n_above + above, k), o.status);
+  }
+  if (!found && t == 0) atomicOr(a.status, TOPK_DEVICE_INTERNAL);
+  uint64_t* fg = reinterpret_cast<uint64_t*>(g->fine);
+  for (int i = t; i < kFineBins / 2; i += kBlock) st_agent(fg + i, (uint64_t)0);
+  for (int r = t; r < kBins; r += kBlock) st_agent(&g->hist[r], 0u);
+  if (t < 4) st_agent(&g->range[t], 0u);
+  if (t == 0) {
+    st_agent(&g->arrive, 0u);
+    st_agent(&g->emit, 0u);
+    st_agent(&g->cand, 0u);
+    st_agent(&g->done, 0u);
+  }
+}
+
 // The last workgroup of a split row resolves its threshold bin from the
 // candidates the row's workgroups left in global memory, then flushes the
 // outputs [n_above, k).
 template <bool VEC>
-__device__ __forceinline__ void resolve_split(const SelectArgs& a, const GroupState* g, const uint64_t* slab,
-                                              bool keep, int32_t len, const float* rowp, Cut cut, uint32_t need,
-                                              uint32_t cnt, uint32_t n_above, Smem& sh, const RowOut& o) {
+__device__ __forceinline__ void resolve_split(const SelectArgs& a, GroupState* g, const uint64_t* slab,
+                                              bool keep, int32_t len, const float* rowp,
+                                              Cut cut, uint32_t need, uint32_t cnt, uint32_t n_above, Smem& sh,
+                                              const RowOut& o) {
   const int t = threadIdx.x;
   if (t == 0) sh.cur_out = n_above;
   if (keep && cnt <= (uint32_t)(kRegSmall * kBlock)) {
     resolve_global_regs<kRegSmall>(g, slab, need, cnt, sh, o);
   } else if (keep && cnt <= (uint32_t)(kRegMid * kBlock)) {
     resolve_global_regs<kRegMid>(g, slab, need, cnt, sh, o);
-  } else if (keep && cnt <= (uint32_t)(kResolveRegs * kBlock)) {
-    resolve_global_regs<kResolveRegs>(g, slab, need, cnt, sh, o);
   } else {
     if (t < 4) sh.range[t] = ld_agent(&g->range[t]);
     __syncthreads();
     const Refine p = make_refine(sh.range, need, cnt);
     if (!keep) {
       refine<false>(StreamSrc<VEC>{rowp, 0, len, cut, p}, p, sh, o);
-    } else if (cnt <= (uint32_t)kListCap) {
-      // Pull the list into LDS as composite keys, kLoadBatch device-coherent
-      // loads in flight per lane, then resolve it there.
-      for (uint32_t i0 = 0; i0 < cnt; i0 += kLoadBatch * kBlock) {
-        uint64_t b[kLoadBatch];
-#pragma unroll
-        for (int j = 0; j < kLoadBatch; ++j) {
-          const uint32_t i = i0 + (uint32_t)j * kBlock + t;
-          b[j] = i < cnt ? ld_agent(slab + i) : 0ull;
-        }
-#pragma unroll
-        for (int j = 0; j < kLoadBatch; ++j) {
-          const uint32_t i = i0 + (uint32_t)j * kBlock + t;
-          if (i < cnt) sh.list[i] = p.key((uint32_t)(b[j] >> 32), (int32_t)(uint32_t)b[j]);
-        }
-      }
+    } else if (cnt <= (uint32_t)(kListCap - kLdsCopyWords)) {
+      // Pull the list into LDS (direct-to-LDS copy: no registers in flight),
+      // rewrite it as composite keys and resolve it there.
+      copy_agent_to_lds(slab, cnt, sh.list);
+      drain_memory();
       __syncthreads();
+      pairs_to_keys(sh, cnt, p);
       refine<true>(KeyListSrc{sh.list, cnt}, p, sh, o);
     } else {
       refine<false>(PairListSrc{slab, cnt, p}, p, sh, o);
@@ -1382,6 +1668,17 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
   const uint32_t local_cnt = found ? uni(sh.lhist[raw_of_bin(bstar)]) : 0u;
   const bool keep = found && (int64_t)cnt <= a.cand_cap;
   const bool stage = keep && local_cnt <= (uint32_t)kStageCap;   // candidates staged in LDS
+  // A large threshold bin (uniform across the row's workgroups): its
+  // candidates are also counted by fine digit, in LDS when the staged list
+  // leaves room for the counters, else straight into the row's global digit
+  // histogram.
+  const bool fine = keep && cnt > kFineMin && cnt <= kFineMaxCand;
+  const bool fine_lds = local_cnt <= (uint32_t)kFineListOff;
+  const Refine pf = fine_key_frame(fine_frame(bstar), (uint32_t)len);
+  const uint32_t dshift = pf.nb - (uint32_t)kFineBits;
+  uint32_t* lfine = reinterpret_cast<uint32_t*>(sh.list + kFineListOff);
+  if (fine && fine_lds)   // (ordered before the counting by the barrier below)
+    for (int i = t; i < kFineBins / 4; i += kBlock) reinterpret_cast<uint4*>(lfine)[i] = make_uint4(0u, 0u, 0u, 0u);
   // This workgroup's output and candidate offsets in the row; their round
   // trips overlap the re-reads of the extraction below.
   // Thread 0 uses the atomics' results only after the extraction (nothing
@@ -1397,8 +1694,10 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
     // address, the compiler turns each fetch-add into its wave-aggregated
     // form, which reads the result back at once and so waits here.
     const uint32_t z = opaque_zero();
-    if (local_above) base_out = __hip_atomic_fetch_add(&g->emit + z, local_above, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (keep && local_cnt) base_cand = __hip_atomic_fetch_add(&g->cand + z, local_cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (local_above && !fine)
+      base_out = __hip_atomic_fetch_add(&g->emit + z, local_above, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (keep && local_cnt && !fine)
+      base_cand = __hip_atomic_fetch_add(&g->cand + z, local_cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (keep && !stage) {
@@ -1421,8 +1720,19 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
   };
   auto on_cand = [&](uint32_t kk, int32_t e) {
     if (!keep) return;
+    // fine rows store the fine-frame composite key, others (key32, position)
+    const uint64_t v = fine ? pf.key(kk, e) : ((uint64_t)kk << 32) | (uint32_t)e;
+    if (fine) {
+      const uint32_t d = min((uint32_t)(v >> dshift), (uint32_t)kFineBins - 1u);
+      if (fine_lds) {
+        // (the first increment of a digit appends it: a uniform-address
+        // append the compiler aggregates per wave)
+        atomicAdd(&lfine[d], 1u);
+      } else {
+        __hip_atomic_fetch_add(&g->fine[d], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
     const uint32_t c = atomicAdd(&sh.cur_list, 1u);
-    const uint64_t v = ((uint64_t)kk << 32) | (uint32_t)e;
     const bool ok = stage ? c < (uint32_t)kStageCap : (int64_t)c < a.cand_cap;
     if (ok && stage) sh.list[c] = v;
     if (ok && !stage) st_agent(slab + c, v);
@@ -1445,6 +1755,10 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
         extract(interest_mask(hk, cut.vlo), base, rowp, cut.vhi, rg, on_above, on_cand, &o);
       }
     }
+  }
+  if (fine) {
+    fine_tail<VEC>(a, g, slab, len, G, k, n_above, cnt, local_above, fine_lds, pf, sh, o, bad);
+    return;
   }
   merge_range(rg, sh);
   __syncthreads();

@@ -58,6 +58,12 @@ struct WorkItem {
 };
 static_assert(sizeof(WorkItem) == 32, "work item is 32 bytes");
 
+// Boundary candidates of a split row are also counted by a 13-bit digit of
+// their FP32 key, in a frame fixed by the threshold bin, so that the last
+// workgroup starts its exact selection from a finished digit histogram.
+constexpr int kFineBits = 13;
+constexpr int kFineBins = 1 << kFineBits;
+
 // Cross-workgroup state of one split row. Left zeroed after every use.
 struct GroupState {
   uint32_t hist[kBins];   // merged 1,024-bin histogram
@@ -67,8 +73,9 @@ struct GroupState {
   uint32_t done;          // workgroups that finished emission
   uint32_t range[4];      // threshold-bin candidates: max key32, ~min key32, max pos, ~min pos
   uint32_t pad[8];
+  uint32_t fine[kFineBins];   // threshold-bin candidates by FP32-key digit (large bins only)
 };
-static_assert(sizeof(GroupState) == 4096 + 64, "group state layout");
+static_assert(sizeof(GroupState) == 4096 + 64 + 4 * kFineBins, "group state layout");
 
 // The device status word sits at workspace offset 0.
 constexpr size_t kStatusBytes = 256;

@@ -515,7 +515,7 @@ def test_device_histogram_and_threshold_bin(workloads, case):
         b, above, cnt = thr[r]
         vk = w.scores[r, ref_idx[r, w.k - 1]]
         assert b == _key16_bins(np.array([vk], np.float32))[0], f"{case} row {r}"
-        assert above == hist[r, b + 1:].sum() and cnt == hist[r, b]
+        assert above == hist[r, b + 1:hi].sum() and cnt == hist[r, b]
         assert above < w.k <= above + cnt
 
 
@@ -523,3 +523,77 @@ def oracle_sorted(w):
     """The oracle's output in its own (score desc, position asc) order."""
     import oracle
     return oracle.topk_workload(w, threads=8)
+
+
+def _large_bin_rows(kind: str, seed: int):
+    """5 split rows of 40,000 scores whose threshold bin (k = 2048) holds
+    between 4,097 and 12,288 candidates: the rows whose boundary is first
+    narrowed by the fine FP32-key digit. Kinds place that bin where the
+    digit frame is narrow (a cluster at 3.0), where one key repeats, and
+    where it is widest: the -inf bin (finite values below -65520 round to
+    -inf in FP16), the zero bin (+-0 and FP32 denormals) and the +inf bin."""
+    st = synth.Stream(seed, 17)
+    rows, n, k = 5, 40_000, 2048
+    # The -inf bin is the lowest: only the 9,000 scores at and above it are valid there.
+    valid = 9_000 if kind == "neg_inf_bin" else n
+    scores = np.empty((rows, n), np.float32)
+    for r in range(rows):
+        row = synth._f32(st.normal(n) - 20.0)               # far below the boundary
+        pos = st.permutation(valid)
+        top, mid = pos[:1000], pos[1000:1000 + 8000]
+        row[top] = synth._f32(st.normal(1000) + 50.0)        # above the boundary bin
+        if kind == "cluster":
+            row[mid] = synth._f32(3.0 + st.below(8000, 600) * 2.0 ** -22)
+        elif kind == "big_tie_front":
+            # as big_tie, all inside the first 16,384 positions: split over two
+            # workgroups, one holds every candidate and more survivors than
+            # its LDS staging takes
+            front = pos[pos < 16_384]
+            top, tie, rest = front[:500], front[500:5500], front[5500:12500]
+            row[top] = synth._f32(st.normal(500) + 50.0)
+            row[tie] = np.float32(7.375)
+            row[rest] = synth._f32(7.375 - (1 + st.below(rest.size, 100_000)) * 2.0 ** -21)
+        elif kind == "big_tie":
+            # 12,000 in the bin [7.25, 7.5): 5,000 copies of the cut value
+            # 7.375 (one fine digit holding the cut, too many to compact past
+            # the list) and 7,000 distinct values just below it in the bin
+            top = pos[:500]
+            row[top] = synth._f32(st.normal(500) + 50.0)
+            tie, rest = pos[500:5500], pos[5500:12500]
+            row[tie] = np.float32(7.375)
+            row[rest] = synth._f32(7.375 - (1 + st.below(7000, 100_000)) * 2.0 ** -21)
+        elif kind == "one_key":
+            row[mid] = np.float32(7.25)
+        elif kind == "neg_inf_bin":
+            v = synth._f32(-1e30 * (1.0 + st.uniform(8000)))
+            v[st.below(8000, 4) == 0] = -np.inf
+            row[mid] = v
+            row[valid:] = np.float32(1e30)                  # junk past the valid length
+        elif kind == "zero_bin":
+            v = synth._f32(st.uniform(8000) * 3.7e-6)
+            sel = st.below(8000, 5)
+            v[sel == 0] = np.float32(0.0)
+            v[sel == 1] = np.float32(-0.0)
+            v[sel == 2] = synth._f32(st.uniform(int((sel == 2).sum())) * 1e-39)   # FP32 denormals
+            row[mid] = v
+        elif kind == "pos_inf_bin":
+            row[top] = synth._f32(st.normal(1000) + 30.0)
+            v = synth._f32(65520.0 * (1.0 + st.uniform(8000)))
+            v[st.below(8000, 8) == 0] = np.inf
+            row[mid] = v
+            row[top] = np.inf if r % 2 else row[top]
+        scores[r] = row
+    lengths = np.full(rows, valid, np.int32)
+    bt = synth.page_permutation_tables(st, rows, (n + 63) // 64)
+    return synth.Workload(f"large_bin_{kind}", scores, lengths, bt, bt.shape[1], 64, k, seed)
+
+
+@pytest.mark.parametrize("kind", ["cluster", "one_key", "big_tie", "big_tie_front", "neg_inf_bin", "zero_bin",
+                                  "pos_inf_bin"])
+@pytest.mark.parametrize("path,kw", [("multi", {"wg_per_row": 2}), ("multi", {"wg_per_row": 8}),
+                                     ("multi", {"wg_per_row": 36})], ids=["wg2", "wg8", "wg36"])
+def test_split_row_large_threshold_bin(kind, path, kw):
+    w = _large_bin_rows(kind, 440 + len(kind))
+    _gpu.say(f"[large bin] {kind} {kw}")
+    for got in _gpu.run_gpu(w, path, repeat=2, **kw):
+        _gpu.assert_matches_oracle(w, got, f"large bin {kind} {kw}")
