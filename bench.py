@@ -325,6 +325,8 @@ def sweep(args) -> int:
                               else "whole batch, median of 3"),
             "cpu": cpu_model(), "nproc": os.cpu_count(), "parity": parity,
         }), flush=True)
+    if args.calibrate_copy_mb:
+        calibrate_copy(args.calibrate_copy_mb)
     return 0 if ok else 1
 
 
