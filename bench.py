@@ -73,7 +73,22 @@ def workload(name: str):
         return synth.make_prefill()
     if name == "plan_split_600":
         return synth.make_plan_split()
+    if name.startswith("c5_g"):
+        # one 64-row group of C5 (0 one value, 1 sixteen values, 2 one FP16
+        # bin, 3 sorted descending), run on the full batch's path (one
+        # workgroup per row): its share of the C5 time
+        g = int(name[4:])
+        w = synth.make_config(5)
+        rows = slice(64 * g, 64 * (g + 1))
+        return synth.Workload(f"c5_group{g}", w.scores[rows], w.lengths[rows], w.block_table[rows],
+                              w.bt_row_stride, w.page_size, w.k, w.seed)
     return synth.make_config(table[name])
+
+
+def path_of(name: str) -> str:
+    """The path a workload is timed on: C5's groups alone would be split, so
+    they keep the whole batch's one workgroup per row."""
+    return "single" if name.startswith("c5_g") else "auto"
 
 
 def row_sample(w, rows: int):
@@ -104,7 +119,7 @@ def algorithmic_bytes(w, slots, with_idx: bool) -> int:
 EVENT_STEPS_MIN = 200   # event-timed steps (outside the timed region) for percentiles
 
 
-def measure(w, steps: int, warmup: int, with_idx: bool = True, rotate: bool = True):
+def measure(w, steps: int, warmup: int, with_idx: bool = True, rotate: bool = True, path: str = "auto"):
     """Time `steps` plan+select steps; returns a dict of timings and the last output.
 
     Two passes. The first is the timed region proper: exactly `steps` steps
@@ -121,7 +136,7 @@ def measure(w, steps: int, warmup: int, with_idx: bool = True, rotate: bool = Tr
     from sparse_attention_indexer_amd import topk
 
     dev = torch.device("cuda:0")
-    tk = topk.TopK(w.k, w.rows, max(1, w.max_len), device=dev)
+    tk = topk.TopK(w.k, w.rows, max(1, w.max_len), force_path=path, device=dev)
     per_copy = max(1, w.scores.nbytes)
     ncopy = max(1, math.ceil(ROTATION_BYTES / per_copy)) if rotate else 1
     base = torch.from_numpy(np.ascontiguousarray(w.scores)).to(dev)
@@ -290,7 +305,7 @@ def sweep(args) -> int:
     for name in names:
         w = workload(name)
         say(f"[bench] sweep {name}: {w.rows}x{w.stride}")
-        res = measure(w, args.steps, args.warmup, rotate=not args.warm_cache)
+        res = measure(w, args.steps, args.warmup, rotate=not args.warm_cache, path=path_of(name))
         nthreads = host_threads(w.rows)
         # the oracle's timing on at most 256 rows (scaled to the batch); its
         # parity result on the whole batch
@@ -310,7 +325,7 @@ def sweep(args) -> int:
         nbytes = algorithmic_bytes(w, res["out"][1], True)
         p50 = res["select_p50_ms"] * 1e-3
         print(json.dumps({
-            "workload": w.name, "rows": w.rows, "stride": w.stride, "k": w.k,
+            "workload": w.name, "rows": w.rows, "stride": w.stride, "k": w.k, "path": path_of(name),
             "select_us": {"p50": round(res["select_p50_ms"] * 1e3, 3), "p10": round(res["select_p10_ms"] * 1e3, 3),
                           "p90": round(res["select_p90_ms"] * 1e3, 3), "mean": round(res["select_ms"] * 1e3, 3)},
             "plan_us": ({"mean": round(res["plan_ms"] * 1e3, 3), "p50": round(res["plan_p50_ms"] * 1e3, 3)}
@@ -345,7 +360,7 @@ def main() -> int:
     ap.add_argument("--no-read-ceiling", action="store_true",
                     help="skip the streaming-read ceiling measurement")
     ap.add_argument("--sweep", default="",
-                    help="comma list from {c1..c5, cp8_7x125k, prefill_4096x80k, plan_split_600}: "
+                    help="comma list from {c1..c5, c5_g0..c5_g3, cp8_7x125k, prefill_4096x80k, plan_split_600}: "
                          "one JSON line per workload")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -823,6 +823,23 @@ __device__ __forceinline__ FineFrame fine_frame(uint32_t b) {
   f.shift = w > (uint32_t)kFineBits ? w - (uint32_t)kFineBits : 0u;
   return f;
 }
+// The composite key of a threshold-bin candidate in its fine digit's frame:
+// ((key32 - lo) << b2) | (len - 1 - position), with b2 = bitwidth(len - 1)
+// and 13 + shift key bits (every candidate's key offset is below
+// 2^(13 + shift)), so its top 13 bits are its fine digit. It depends on the
+// threshold bin and the row length alone, so every workgroup of a split row
+// derives the same one; their producers store candidates in this form.
+__device__ __forceinline__ Refine fine_key_frame(FineFrame fr, uint32_t len) {
+  Refine p;
+  p.lo32 = fr.lo;
+  p.idx_hi = len - 1u;
+  p.b2 = bit_width(len - 1u);
+  p.nb = (uint32_t)kFineBits + fr.shift + p.b2;
+  p.need = 0;
+  p.cnt = 0;
+  return p;
+}
+
 // Split rows whose threshold bin holds more candidates than this count them
 // by fine digit as they classify (below it the last workgroup's register pass
 // is cheap), up to what that pass holds in registers.
@@ -921,9 +938,13 @@ struct StreamSrc {
 // Outputs are staged from sh.cur_out onwards. SRC_IN_LDS: the source is the
 // composite-key list sh.list[0, n0). The search may resume after `pbits0`
 // key bits already fixed to `prefix0`, with `need0` still to select.
+// `counted`: the first pass's 13-bit histogram (padded, at the start of the
+// list region) was already filled while the source was classified, so the
+// first pass only emits and compacts (streamed sources, pbits0 == 0).
 template <bool SRC_IN_LDS, class Src>
 __device__ __forceinline__ void refine(const Src& src, const Refine& p, Smem& sh, const RowOut& o,
-                                       uint64_t prefix0, uint32_t pbits0, uint32_t need0, uint32_t n0) {
+                                       uint64_t prefix0, uint32_t pbits0, uint32_t need0, uint32_t n0,
+                                       bool counted = false) {
   const int t = threadIdx.x;
   bool bad = false;
   if (need0 == n0) {
@@ -955,17 +976,20 @@ __device__ __forceinline__ void refine(const Src& src, const Refine& p, Smem& sh
     const uint32_t top = shift + width;   // <= 63
     const uint32_t mask = (1u << width) - 1u;
     const uint32_t words = wide ? (mask + 1) + ((mask + 1) >> kWidePad) : mask + 1;
-    for (int i = t; i < (int)words; i += kBlock) hist[i] = 0;
-    __syncthreads();
-    // Digits mix key and position bits, so hot bins are rare: plain atomics.
-    auto hist_fn = [&](bool valid, uint64_t ck) {
-      if (valid && (ck >> top) == prefix) {
-        const uint32_t d = (uint32_t)(ck >> shift) & mask;
-        atomicAdd(&hist[wide ? d + (d >> kWidePad) : d], 1u);
-      }
-    };
-    if (in_list) KeyListSrc{sh.list + list_off, list_n}.each(hist_fn);
-    else src.each(hist_fn);
+    if (!counted) {
+      for (int i = t; i < (int)words; i += kBlock) hist[i] = 0;
+      __syncthreads();
+      // Digits mix key and position bits, so hot bins are rare: plain atomics.
+      auto hist_fn = [&](bool valid, uint64_t ck) {
+        if (valid && (ck >> top) == prefix) {
+          const uint32_t d = (uint32_t)(ck >> shift) & mask;
+          atomicAdd(&hist[wide ? d + (d >> kWidePad) : d], 1u);
+        }
+      };
+      if (in_list) KeyListSrc{sh.list + list_off, list_n}.each(hist_fn);
+      else src.each(hist_fn);
+    }
+    counted = false;
     __syncthreads();
     if (t == 0) sh.res[0] = kNotFound;
     if (wide) find_threshold<kFirstRadixBins / kBlock, kWidePad>(hist, (int)(mask + 1), need, sh.scratch, sh.res);
@@ -1158,7 +1182,83 @@ __device__ __forceinline__ void resolve_lds_pairs(uint32_t n, const Refine& p, S
 // A row the workgroup owns alone: register path when the row fits one tile,
 // streaming path otherwise. Selected positions are staged in LDS and the
 // row's k outputs flushed once at the end.
+// Threshold-bin candidates that all hold one FP32 key (so one score): the
+// `need` of them at the lowest positions are the selected ones. One pass in
+// position order, kFirstGroups vector groups (kFirstGroups * 2,048
+// positions) per step: a step whose candidates all fit the remaining need is
+// emitted whole; in the step where the count is reached its vector groups
+// are ranked one at a time (group q holds positions [2048 q, 2048 (q + 1))
+// of the step, lane-major). The pass stops there, so the rest of the row is
+// not read. Output slots come from block scans of the lanes' counts.
+constexpr int kFirstGroups = 4;
 template <bool VEC>
+__device__ __forceinline__ void first_need(const float* rowp, int32_t len, Cut cut, uint32_t need, Smem& sh,
+                                           const RowOut& o) {
+  constexpr int32_t kStepLen = kFirstGroups * kBlock * 4;
+  bool bad = false;
+#pragma unroll 1
+  for (int32_t base = 0; base < len && need > 0; base += kStepLen) {
+    float4 x[kFirstGroups];
+#pragma unroll
+    for (int u = 0; u < kFirstGroups; ++u) {
+      const int32_t e = tile_pos(base, u, 0);
+      x[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (VEC) {
+        if (e < len) x[u] = *reinterpret_cast<const float4*>(rowp + e);
+      } else {
+        if (e < len) x[u].x = rowp[e];
+        if (e + 1 < len) x[u].y = rowp[e + 1];
+        if (e + 2 < len) x[u].z = rowp[e + 2];
+        if (e + 3 < len) x[u].w = rowp[e + 3];
+      }
+    }
+    // bit 4 u + j: the lane's position tile_pos(base, u, j) is a candidate
+    uint32_t m = 0;
+#pragma unroll
+    for (int u = 0; u < kFirstGroups; ++u) {
+      const int32_t e = tile_pos(base, u, 0);
+      const float v[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const _Float16 h = half_lo(to_half2(v[j], v[j]));
+        m |= (e + j < len && h >= cut.vlo && !(h >= cut.vhi)) ? 1u << (4 * u + j) : 0u;
+      }
+    }
+    const uint32_t cur = uni(sh.cur_out);
+    uint32_t tot;
+    uint32_t pos = cur + block_exclusive_add((uint32_t)__popc(m), sh.scratch, &tot);
+    tot = uni(tot);
+    if (tot <= need) {
+      for (uint32_t mm = m; mm != 0; mm &= mm - 1) {
+        const int b = __builtin_ctz(mm);
+        bad |= !o.write(pos++, tile_pos(base, b >> 2, b & 3));
+      }
+      if (threadIdx.x == 0) sh.cur_out = cur + tot;
+      need -= tot;
+      __syncthreads();
+      continue;
+    }
+    uint32_t done = 0;
+#pragma unroll 1
+    for (int u = 0; u < kFirstGroups && done < need; ++u) {
+      const uint32_t mu = (m >> (4 * u)) & 0xFu;
+      uint32_t tu;
+      uint32_t r = done + block_exclusive_add((uint32_t)__popc(mu), sh.scratch, &tu);
+      for (uint32_t mm = mu; mm != 0; mm &= mm - 1) {
+        const int j = __builtin_ctz(mm);
+        if (r < need) bad |= !o.write(cur + r, tile_pos(base, u, j));
+        ++r;
+      }
+      done += uni(tu);
+    }
+    if (threadIdx.x == 0) sh.cur_out = cur + need;
+    need = 0;
+  }
+  report_bad(bad, o.status);
+  __syncthreads();
+}
+
+template <bool VEC, bool STREAM>
 __device__ __forceinline__ void owned_row(const SelectArgs& a, int32_t len, const float* rowp, const RowOut& o,
                                           bool resident, uint32_t (&hk)[kHk], Smem& sh) {
   if (threadIdx.x == 0) sh.res[0] = kNotFound;
@@ -1170,6 +1270,16 @@ __device__ __forceinline__ void owned_row(const SelectArgs& a, int32_t len, cons
   }
   const Cut cut = cut_of_bin(bstar);
   const bool use_list = cnt <= (uint32_t)kListCap;
+  // Too many candidates for the list: they are counted by the 13-bit digit of
+  // their composite key in the threshold bin's fine frame as they are
+  // classified, into the padded histogram the exact selection's first pass
+  // uses (at the start of the free list region), so that pass needs no count
+  // of its own over the row.
+  const Refine pf = fine_key_frame(fine_frame(bstar), (uint32_t)len);
+  const uint32_t dshift = pf.nb - (uint32_t)kFineBits;
+  uint32_t* whist = reinterpret_cast<uint32_t*>(sh.list);
+  if (!use_list)
+    for (int i = threadIdx.x; i < kWideWords; i += kBlock) whist[i] = 0;
   if (threadIdx.x == 0) {
     sh.cur_out = 0;
     sh.cur_list = 0;
@@ -1185,6 +1295,10 @@ __device__ __forceinline__ void owned_row(const SelectArgs& a, int32_t len, cons
       const bool ok = c < (uint32_t)kListCap;
       if (ok) sh.list[c] = ((uint64_t)kk << 32) | (uint32_t)e;
       bad |= !ok;
+    } else {
+      // (one add per wave when its lanes share the digit: single-key rows)
+      const uint32_t d = (uint32_t)(pf.key(kk, e) >> dshift);
+      hist_add(whist, true, d + (d >> kWidePad));
     }
   };
   if (resident) {
@@ -1216,18 +1330,28 @@ __device__ __forceinline__ void owned_row(const SelectArgs& a, int32_t len, cons
   merge_range(rg, sh);
   report_bad(bad, a.status);
   __syncthreads();
-  const Refine p = make_refine(sh.range, (uint32_t)a.k - n_above, cnt);
-  if (use_list && cnt <= (uint32_t)(kRegSmall * kBlock)) {
+  const uint32_t need = (uint32_t)a.k - n_above;
+  const Refine p = make_refine(sh.range, need, cnt);
+  if (STREAM && !resident && !use_list && uni(sh.range[0]) == ~uni(sh.range[1])) {
+    // Every candidate holds the same FP32 key: the lowest positions win.
+    // (Streamed rows only: in a row of one tile the fine-digit passes below
+    // cost a tile read each, and the extra pass would only add registers to
+    // the kernels that serve such rows.)
+    if constexpr (STREAM) first_need<VEC>(rowp, len, cut, need, sh, o);
+  } else if (!use_list) {
+    Refine q = pf;
+    q.need = need;
+    q.cnt = cnt;
+    refine<false>(StreamSrc<VEC>{rowp, 0, len, cut, q}, q, sh, o, 0ull, 0u, need, cnt, true);
+  } else if (cnt <= (uint32_t)(kRegSmall * kBlock)) {
     resolve_lds_pairs<kRegSmall>(cnt, p, sh, o);
-  } else if (use_list && cnt <= (uint32_t)(kRegMid * kBlock)) {
+  } else if (cnt <= (uint32_t)(kRegMid * kBlock)) {
     resolve_lds_pairs<kRegMid>(cnt, p, sh, o);
-  } else if (use_list && cnt <= (uint32_t)(kResolveRegs * kBlock)) {
+  } else if (cnt <= (uint32_t)(kResolveRegs * kBlock)) {
     resolve_lds_pairs<kResolveRegs>(cnt, p, sh, o);
-  } else if (use_list) {
+  } else {
     pairs_to_keys(sh, cnt, p);
     refine<true>(KeyListSrc{sh.list, cnt}, p, sh, o);
-  } else {
-    refine<false>(StreamSrc<VEC>{rowp, 0, len, cut, p}, p, sh, o);
   }
   report_bad(!o.flush(0, (uint32_t)a.k), a.status);
 }
@@ -1287,23 +1411,6 @@ constexpr uint32_t kFineMaxCand = kResolveRegs * kBlock;      // 12,288 candidat
 constexpr uint32_t kFineHistEntry = kFineMaxCand;             // ... then the digit counts
 static_assert(kFineHistEntry + kFineBins / 2 <= (uint32_t)kListCap, "candidates and digit counts share the LDS list");
 static_assert(kFineMaxCand % kLdsCopyWords == 0, "the rounded-up copy stays below the digit counts");
-
-// The composite key of a threshold-bin candidate of a split row in its fine
-// digit's frame: ((key32 - lo) << b2) | (len - 1 - position), with
-// b2 = bitwidth(len - 1) and 13 + shift key bits (every candidate's key
-// offset is below 2^(13 + shift)), so its top 13 bits are its fine digit.
-// Every workgroup of the row derives it from the threshold bin and the row
-// length alone; the producers store candidates in this form.
-__device__ __forceinline__ Refine fine_key_frame(FineFrame fr, uint32_t len) {
-  Refine p;
-  p.lo32 = fr.lo;
-  p.idx_hi = len - 1u;
-  p.b2 = bit_width(len - 1u);
-  p.nb = (uint32_t)kFineBits + fr.shift + p.b2;
-  p.need = 0;
-  p.cnt = 0;
-  return p;
-}
 
 // Every workgroup of a split row whose threshold bin holds more than
 // kFineMin candidates ("fine" rows), after classifying its chunk: its
@@ -1903,7 +2010,7 @@ __device__ __forceinline__ void process_item(const SelectArgs& a, const WorkItem
   __syncthreads();
   hist_copies_sum(hc, sh.lhist);
   __syncthreads();
-  if (w.group < 0) owned_row<VEC>(a, len, rowp, o, resident, hk, sh);
+  if (w.group < 0) owned_row<VEC, STREAM>(a, len, rowp, o, resident, hk, sh);
   else split_row<VEC>(a, w, len, rowp, o, resident, hk, sh);
 }
 

@@ -597,3 +597,48 @@ def test_split_row_large_threshold_bin(kind, path, kw):
     _gpu.say(f"[large bin] {kind} {kw}")
     for got in _gpu.run_gpu(w, path, repeat=2, **kw):
         _gpu.assert_matches_oracle(w, got, f"large bin {kind} {kw}")
+
+
+def _owned_large_bin_rows(kind: str, seed: int):
+    """4 rows of 140,000 scores (250,000 for "sparse_extract") selected by one
+    streamed workgroup each, whose threshold bin holds more candidates than
+    the LDS list (16,384): counted by fine digit while classified, or, when
+    they all hold one key, taken in position order."""
+    st = synth.Stream(seed, 23)
+    rows, k = 4, 2048
+    n = 250_000 if kind == "sparse_extract" else 140_000
+    scores = np.empty((rows, n), np.float32)
+    for r in range(rows):
+        row = synth._f32(st.normal(n) - 10.0)                 # far below the boundary
+        pos = st.permutation(n)
+        n_top = [0, 500, 1000, 2047][r]                      # row 3: one candidate needed
+        row[pos[:n_top]] = synth._f32(st.normal(n_top) + 100.0)
+        rest = pos[n_top:]
+        if kind == "one_key_scattered":                      # 30,000 copies anywhere
+            row[rest[:30_000]] = np.float32(5.0)
+        elif kind == "one_key_late":                         # 20,000 copies, all past position 90,000
+            late = rest[rest >= 90_000][:20_000]
+            row[late] = np.float32(5.0)
+        elif kind == "one_key_whole_row":                    # every other score is the key
+            row[rest] = np.float32(5.0)
+        elif kind == "hot_digit":                            # 18,000 copies of 5.0 and 1,500 just above
+            row[rest[:18_000]] = np.float32(5.0)
+            row[rest[18_000:19_500]] = synth._f32(5.0 + (1 + st.below(1500, 3000)) * 2.0 ** -20)
+        elif kind == "one_bin_distinct":                     # 8,192 values of one FP16 bin, ~17 copies each
+            row[rest] = synth._f32(1.0 + st.below(rest.size, 8192) * 2.0 ** -23)
+        elif kind == "sparse_extract":                       # 20,000 of 250,000: re-binned, not re-read whole
+            row[rest[:20_000]] = synth._f32(3.0 + st.below(20_000, 2000) * 2.0 ** -22)
+        scores[r] = row
+    lengths = np.full(rows, n, np.int32)
+    bt = synth.page_permutation_tables(st, rows, (n + 63) // 64)
+    return synth.Workload(f"owned_large_bin_{kind}", scores, lengths, bt, bt.shape[1], 64, k, seed)
+
+
+@pytest.mark.parametrize("kind", ["one_key_scattered", "one_key_late", "one_key_whole_row", "hot_digit",
+                                  "one_bin_distinct", "sparse_extract"])
+@pytest.mark.parametrize("offset", [0, 1], ids=["aligned", "unaligned"])
+def test_owned_row_large_threshold_bin(kind, offset):
+    w = _owned_large_bin_rows(kind, 610 + len(kind))
+    _gpu.say(f"[owned large bin] {kind} offset {offset}")
+    for got in _gpu.run_gpu(w, "single", scores_offset=offset, repeat=2):
+        _gpu.assert_matches_oracle(w, got, f"owned large bin {kind} offset {offset}")
