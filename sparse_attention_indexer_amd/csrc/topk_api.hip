@@ -3,6 +3,7 @@
 // here except in topk_read_status, which says so.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "sparse_topk.h"
@@ -31,32 +32,39 @@ using namespace satopk;
 namespace {
 
 // Per-device CU count and co-resident selection workgroups per CU. This cache
-// is the library's only global state; it never changes once filled.
+// is the library's only global state; it never changes once filled. Filled
+// under a lock once per device; every later call reads it without one (the
+// release store of `ready` publishes the two counts).
 struct DevInfo {
   int cus = 0;
   int per_cu = 0;
-  bool ready = false;
+};
+struct DevSlot {
+  std::atomic<bool> ready{false};
+  DevInfo info;
 };
 constexpr int kMaxDevices = 64;
-DevInfo g_dev[kMaxDevices];
+DevSlot g_dev[kMaxDevices];
 std::mutex g_dev_mu;
 
 topk_status device_info(DevInfo* out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TOPK_ERR_HIP;
-  std::lock_guard<std::mutex> lock(g_dev_mu);
-  DevInfo& d = g_dev[dev];
-  if (!d.ready) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      return TOPK_ERR_HIP;
-    int per_cu = 0;
-    if (select_occupancy(&per_cu) != hipSuccess || per_cu <= 0) return TOPK_ERR_HIP;
-    d.cus = cus;
-    d.per_cu = per_cu;
-    d.ready = true;
+  DevSlot& d = g_dev[dev];
+  if (!d.ready.load(std::memory_order_acquire)) {
+    std::lock_guard<std::mutex> lock(g_dev_mu);
+    if (!d.ready.load(std::memory_order_relaxed)) {
+      int cus = 0;
+      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return TOPK_ERR_HIP;
+      int per_cu = 0;
+      if (select_occupancy(&per_cu) != hipSuccess || per_cu <= 0) return TOPK_ERR_HIP;
+      d.info.cus = cus;
+      d.info.per_cu = per_cu;
+      d.ready.store(true, std::memory_order_release);
+    }
   }
-  *out = d;
+  *out = d.info;
   return TOPK_OK;
 }
 

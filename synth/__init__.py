@@ -352,3 +352,105 @@ def random_case(seed: int, rows: int, max_len: int, *, k: int | None = None,
     if k is None:
         k = int(st.below(1, 2048)[0]) + 1
     return Workload(f"rand{seed}", scores, lengths, bt, bt_stride, page_size, k, seed)
+
+
+# --- indexer key prologue inputs ---------------------------------------------
+
+@dataclasses.dataclass
+class KeyPrologueInputs:
+    """One batch of new key tokens for the indexer key prologue.
+
+    k_act:        uint16 [tokens, k_stride] BF16 bit patterns; the first `dim`
+                  of each row are the token's key activations.
+    weight, bias: float32 [dim] LayerNorm parameters.
+    cos_sin:      float32 [max_pos, rope_dim]: per position, the cosines of the
+                  rope_dim / 2 pair angles, then their sines (the rotary cache).
+    positions:    int32 [tokens]; token_row: int32 [tokens] (-1 = padding).
+    block_table:  int32 [rows, pages] (bt_row_stride = pages), or [1, pages]
+                  shared (bt_row_stride = 0).
+    num_slots:    physical cache slots (pages in the pool x page_size).
+    """
+    name: str
+    k_act: np.ndarray
+    dim: int
+    weight: np.ndarray
+    bias: np.ndarray
+    eps: float
+    cos_sin: np.ndarray
+    rope_dim: int
+    positions: np.ndarray
+    token_row: np.ndarray
+    block_table: np.ndarray
+    bt_row_stride: int
+    page_size: int
+    num_slots: int
+    seed: int
+
+    @property
+    def tokens(self) -> int:
+        return int(self.positions.shape[0])
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float64 -> BF16 bit patterns, round to nearest even (via FP32)."""
+    f = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rnd = ((f >> np.uint64(16)) & np.uint64(1)) + np.uint64(0x7FFF)
+    return ((f + rnd) >> np.uint64(16)).astype(np.uint16)
+
+
+def rotary_table(max_pos: int, rope_dim: int, base: float = 10000.0) -> np.ndarray:
+    """The serving engines' rotary cache: angle of pair i at position p is
+    p * base^(-2i / rope_dim); row p = [cos of the pairs, sin of the pairs],
+    evaluated in float64 and rounded to float32."""
+    if rope_dim == 0:
+        return np.zeros((max_pos, 0), np.float32)
+    inv = base ** (-np.arange(0, rope_dim, 2, dtype=np.float64) / rope_dim)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+def make_key_prologue(tokens: int, seed: int = 11, *, dim: int = 128, rope_dim: int = 64,
+                      rows: int = 1, page_size: int = 64, k_stride: int | None = None,
+                      pad_every: int = 0, max_pos: int | None = None, shared_table: bool = False,
+                      act_scale: float = 3.0) -> KeyPrologueInputs:
+    """`tokens` new key tokens spread over `rows` requests; request r's tokens
+    take consecutive positions from a random prefix (a chunk of prefill, or a
+    few verify tokens of decode). Activations are N(0, act_scale^2) plus a
+    per-token offset (so LayerNorm has a mean to remove) and a few outlier
+    channels, rounded to BF16. Every request owns a random set of physical
+    pages of one shared pool; `pad_every` > 0 marks every pad_every-th token as
+    padding (row -1)."""
+    st = Stream(seed, 31)
+    ks = dim if k_stride is None else k_stride
+    x = st.normal(tokens * dim).reshape(tokens, dim) * act_scale
+    x += st.normal(tokens)[:, None] * 0.5
+    hot = st.below(4, dim)
+    x[:, hot] *= 8.0
+    k_act = np.zeros((tokens, ks), np.uint16)
+    k_act[:, :dim] = bf16_bits(x)
+    weight = _f32(1.0 + 0.1 * st.normal(dim))
+    bias = _f32(0.05 * st.normal(dim))
+    # tokens split as evenly as possible over rows, consecutive positions each
+    per = np.full(rows, tokens // rows, np.int64)
+    per[: tokens % rows] += 1
+    start = st.below(rows, 4096) if rows > 1 or tokens < 4096 else np.zeros(1, np.int64)
+    token_row = np.repeat(np.arange(rows, dtype=np.int64), per)
+    positions = np.concatenate([start[r] + np.arange(per[r]) for r in range(rows)]) if tokens else \
+        np.zeros(0, np.int64)
+    need_pos = int(positions.max()) + 1 if tokens else 1
+    mp = max(need_pos, max_pos or 0)
+    cos_sin = rotary_table(mp, rope_dim)
+    pages = (mp + page_size - 1) // page_size
+    if shared_table:
+        pool = pages
+        bt = st.permutation(pool)[None, :].astype(np.int32)
+        stride = 0
+    else:
+        pool = rows * pages
+        bt = st.permutation(pool).reshape(rows, pages).astype(np.int32)
+        stride = pages
+    if pad_every > 0:
+        token_row[::pad_every] = -1
+    return KeyPrologueInputs(f"key_prologue_{tokens}t_{rows}r", k_act, dim, weight, bias, 1e-6, cos_sin,
+                             rope_dim, positions.astype(np.int32), token_row.astype(np.int32), bt, stride,
+                             page_size, pool * page_size, seed)
