@@ -296,6 +296,101 @@ def cpu_model() -> str:
     return "unknown"
 
 
+def key_prologue_bytes(w) -> int:
+    """Algorithmic bytes of one key-prologue launch: per live token its BF16
+    activations (2 x 128), position and row (8) and its cache row (128 FP8 +
+    a 4-byte scale); padding tokens their row index only; once, the LayerNorm
+    parameters, the rotary rows of the distinct positions (4 x rope_dim each)
+    and the distinct block-table entries the tokens touch."""
+    import numpy as np
+    live = w.token_row >= 0
+    n = int(live.sum())
+    pages = set(zip(w.token_row[live].tolist(), (w.positions[live] // w.page_size).tolist()))
+    n_pos = int(np.unique(w.positions[live]).size)
+    return (n * (2 * w.dim + 8 + w.dim + 4) + 4 * int((~live).sum()) + 8 * w.dim + 4 * len(pages)
+            + 4 * w.rope_dim * n_pos)
+
+
+def measure_key_prologue(w, steps: int, warmup: int) -> dict:
+    """Event-timed launches of the key prologue (inputs resident; a fresh
+    cache per copy so that writes are not absorbed by a hot cache line);
+    returns percentiles and the last cache contents."""
+    import numpy as np
+    import torch
+    from sparse_attention_indexer_amd import prologue as K
+    dev = torch.device("cuda:0")
+    k_act = torch.from_numpy(w.k_act.view(np.int16)).to(dev)
+    weight, bias = torch.from_numpy(w.weight).to(dev), torch.from_numpy(w.bias).to(dev)
+    cs = torch.from_numpy(w.cos_sin).to(dev) if w.rope_dim else None
+    pos, row = torch.from_numpy(w.positions).to(dev), torch.from_numpy(w.token_row).to(dev)
+    table = torch.from_numpy(np.ascontiguousarray(w.block_table)).to(dev)
+    per_copy = w.k_act.nbytes + w.cos_sin.nbytes
+    ncopy = min(64, max(1, math.ceil(ROTATION_BYTES / max(1, per_copy))))
+    acts = [k_act] + [k_act.clone() for _ in range(ncopy - 1)]
+    cache = torch.zeros((w.num_slots, w.dim), dtype=torch.uint8, device=dev)
+    scale = torch.zeros(w.num_slots, dtype=torch.float32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def launch(i):
+        K.indexer_key_prologue(acts[i % ncopy], weight, bias, w.eps, cs, w.rope_dim, pos, row, table,
+                               w.bt_row_stride, w.page_size, cache, scale, status)
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        launch(i)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) / max(1, steps) * 1e3
+    n_ev = max(steps, EVENT_STEPS_MIN)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        launch(i)
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in evs])
+    return {"wall_ms": wall_ms, "p50_ms": float(np.percentile(t, 50)), "p10_ms": float(np.percentile(t, 10)),
+            "p90_ms": float(np.percentile(t, 90)), "mean_ms": float(t.mean()), "copies": ncopy,
+            "cache": cache.cpu().numpy(), "scale": scale.cpu().numpy(), "status": int(status.item())}
+
+
+def sweep_key_prologue(name: str, args) -> bool:
+    import numpy as np
+    import synth
+    from oracle import prologue as OP
+    tokens = {"key_prologue_128k": 131_072, "key_prologue_7": 7}[name]
+    w = synth.make_key_prologue(tokens, seed=12, rows=8 if tokens > 8 else 1)
+    say(f"[bench] sweep {name}: {tokens} tokens")
+    res = measure_key_prologue(w, args.steps, args.warmup)
+    t = time.perf_counter()
+    slots, codes, scales, _, scaled = OP.key_prologue(w.k_act[:, :w.dim], w.weight, w.bias, w.eps, w.cos_sin,
+                                                      w.rope_dim, w.positions, w.token_row, w.block_table,
+                                                      w.bt_row_stride, w.page_size)
+    t_oracle = time.perf_counter() - t
+    live = slots >= 0
+    got = res["cache"][slots[live]]
+    exact = int((got != codes[live]).sum())
+    srel = float(np.max(np.abs(res["scale"][slots[live]] - scales[live]) / scales[live]))
+    parity = res["status"] == 0 and srel <= 1e-5 and exact <= max(4, got.size // 1000)
+    nbytes = key_prologue_bytes(w)
+    p50 = res["p50_ms"] * 1e-3
+    print(json.dumps({
+        "workload": name, "tokens": tokens, "dim": w.dim, "rope_dim": w.rope_dim, "page_size": w.page_size,
+        "kernel_us": {"p50": round(res["p50_ms"] * 1e3, 3), "p10": round(res["p10_ms"] * 1e3, 3),
+                      "p90": round(res["p90_ms"] * 1e3, 3), "mean": round(res["mean_ms"] * 1e3, 3)},
+        "timing": "stream events around each launch (one kernel), 200 launches",
+        "step_us": round(res["wall_ms"] * 1e3, 3), "tokens_per_s": round(tokens / p50),
+        "algorithmic_bytes": nbytes, "gbs": round(nbytes / p50 / 1e9, 1),
+        "frac_of_8tbs": round(nbytes / p50 / 1e9 / PEAK_HBM_GBS, 4),
+        "cache": f"cold activations ({res['copies']} copies)", "oracle_1thread_s": round(t_oracle, 4),
+        "codes_at_rounding_ties": exact, "scale_max_rel_err": srel, "parity": parity,
+        "cpu": cpu_model(), "nproc": os.cpu_count(),
+    }), flush=True)
+    return parity
+
+
 def sweep(args) -> int:
     """One JSON line per workload: latency percentiles, rows/s, algorithmic GB/s,
     plan time, parity and the oracle's wall time (1 thread and N threads)."""
@@ -303,6 +398,9 @@ def sweep(args) -> int:
     ok = True
     names = args.sweep.split(",")
     for name in names:
+        if name.startswith("key_prologue"):
+            ok &= sweep_key_prologue(name, args)
+            continue
         w = workload(name)
         say(f"[bench] sweep {name}: {w.rows}x{w.stride}")
         res = measure(w, args.steps, args.warmup, rotate=not args.warm_cache, path=path_of(name))
@@ -360,7 +458,8 @@ def main() -> int:
     ap.add_argument("--no-read-ceiling", action="store_true",
                     help="skip the streaming-read ceiling measurement")
     ap.add_argument("--sweep", default="",
-                    help="comma list from {c1..c5, c5_g0..c5_g3, cp8_7x125k, prefill_4096x80k, plan_split_600}: "
+                    help="comma list from {c1..c5, c5_g0..c5_g3, cp8_7x125k, prefill_4096x80k, plan_split_600, "
+                         "key_prologue_128k, key_prologue_7}: "
                          "one JSON line per workload")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))

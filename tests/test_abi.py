@@ -10,12 +10,17 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sparse_topk.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(topk_[a-z0-9_]+)\s*\(", src)))
+    """Every function any include/*.h declares (comments stripped)."""
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b((?:topk|indexer)_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -30,7 +35,7 @@ def test_header_declares_the_boundary():
     for n in ("topk_query_sizes", "topk_plan", "topk_select_paged", "topk_workspace_init",
               "topk_read_status", "topk_status_string", "topk_register_capacity", "topk_debug_keys",
               "topk_debug_stream_read", "topk_stream_read_groups",
-              "topk_select_paged_timed", "topk_debug_histogram"):
+              "topk_select_paged_timed", "topk_debug_histogram", "indexer_key_prologue", "indexer_debug_fp8"):
         assert n in names
 
 
@@ -129,3 +134,52 @@ def test_binding_rejects_strided_lengths_and_tables(T):
         T._select_args(cfg, None, None, lengths, ok_table, 0, 64, None, None, None, None)
     with pytest.raises(ValueError, match="block_table"):
         T._select_args(cfg, None, None, lengths.contiguous(), table, 8, 64, None, None, None, None)
+
+
+# --- the key prologue's host checks --------------------------------------------
+
+def _key_cfg(**kw):
+    from sparse_attention_indexer_amd import prologue as K
+    base = dict(dim=128, rope_dim=64, eps=1e-6, page_size=64, max_pos=1000)
+    base.update(kw)
+    return K.indexer_key_config(base["dim"], base["rope_dim"], base["eps"], base["page_size"], base["max_pos"],
+                                (ctypes.c_int32 * 3)())
+
+
+@pytest.mark.parametrize("kw", [dict(dim=64), dict(rope_dim=12), dict(rope_dim=136), dict(rope_dim=-8),
+                                dict(page_size=0), dict(max_pos=0), dict(eps=-1.0), dict(eps=float("nan")),
+                                dict(eps=float("inf"))])
+def test_key_prologue_bad_config_rejected_without_gpu(T, kw):
+    from sparse_attention_indexer_amd import prologue as K
+    lib = K._lib()
+    buf = (ctypes.c_uint8 * 4096)()
+    p = ctypes.addressof(buf)
+    p16 = p + (-p % 16)
+    cfg = _key_cfg(**kw)
+    st = lib.indexer_key_prologue(ctypes.byref(cfg), p16, 128, 4, p16, p16, p16, p16, None, p16, 0, p16, p16,
+                                  8, None, None)
+    assert st == T.TOPK_ERR_INVALID_ARG
+
+
+def test_key_prologue_bad_arguments_rejected_without_gpu(T):
+    from sparse_attention_indexer_amd import prologue as K
+    lib = K._lib()
+    buf = (ctypes.c_uint8 * 4096)()
+    p = ctypes.addressof(buf)
+    a = p + (-p % 16)
+    cfg = _key_cfg()
+    call = lambda *args: lib.indexer_key_prologue(ctypes.byref(cfg), *args)   # noqa: E731
+    ok = [a, 128, 4, a, a, a, a, None, a, 0, a, a, 8, None, None]
+    bad = [
+        (1, 120), (1, 130), (2, -1), (0, None), (3, None), (5, None), (8, None), (10, None), (11, None),
+        (12, 0), (9, -1), (0, a + 2), (10, a + 8),
+    ]
+    for i, v in bad:
+        args = list(ok)
+        args[i] = v
+        assert call(*args) == T.TOPK_ERR_INVALID_ARG, (i, v)
+    args = list(ok)
+    args[2] = 0
+    assert call(*args) == T.TOPK_OK                       # no tokens: nothing to do, nothing enqueued
+    assert lib.indexer_debug_fp8(None, 5, None, None) == T.TOPK_ERR_INVALID_ARG
+    assert lib.indexer_debug_fp8(None, 0, None, None) == T.TOPK_OK

@@ -120,7 +120,7 @@ def test_rope_dot_products_depend_on_position_difference():
     def dot(m, n):
         a = P.rope_interleaved(q[None, :], cos[m:m + 1], sin[m:m + 1])
         b = P.rope_interleaved(k[None, :], cos[n:n + 1], sin[n:n + 1])
-        return float(a @ b.T)
+        return float((a @ b.T).item())
 
     for m, n, d in [(5, 3, 100), (0, 7, 250), (30, 30, 1)]:
         assert abs(dot(m, n) - dot(m + d, n + d)) < 1e-9
