@@ -1276,7 +1276,9 @@ __device__ __forceinline__ void owned_row(const SelectArgs& a, int32_t len, cons
   // uses (at the start of the free list region), so that pass needs no count
   // of its own over the row.
   const Refine pf = fine_key_frame(fine_frame(bstar), (uint32_t)len);
-  const uint32_t dshift = pf.nb - (uint32_t)kFineBits;
+  // (the digit, the composite key's top 13 bits, is the key offset's top
+  // bits: the position bits lie below them)
+  const uint32_t fshift = pf.nb - (uint32_t)kFineBits - pf.b2;
   uint32_t* whist = reinterpret_cast<uint32_t*>(sh.list);
   if (!use_list)
     for (int i = threadIdx.x; i < kWideWords; i += kBlock) whist[i] = 0;
@@ -1297,7 +1299,7 @@ __device__ __forceinline__ void owned_row(const SelectArgs& a, int32_t len, cons
       bad |= !ok;
     } else {
       // (one add per wave when its lanes share the digit: single-key rows)
-      const uint32_t d = (uint32_t)(pf.key(kk, e) >> dshift);
+      const uint32_t d = (kk - pf.lo32) >> fshift;
       hist_add(whist, true, d + (d >> kWidePad));
     }
   };
