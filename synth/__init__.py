@@ -454,3 +454,76 @@ def make_key_prologue(tokens: int, seed: int = 11, *, dim: int = 128, rope_dim: 
     return KeyPrologueInputs(f"key_prologue_{tokens}t_{rows}r", k_act, dim, weight, bias, 1e-6, cos_sin,
                              rope_dim, positions.astype(np.int32), token_row.astype(np.int32), bt, stride,
                              page_size, pool * page_size, seed)
+
+
+# --- indexer score (MQA logits) inputs ---------------------------------------
+
+@dataclasses.dataclass
+class LogitsInputs:
+    """Query tokens and a paged FP8 key cache for the indexer's MQA logits.
+
+    q_bf16:   uint16 [tokens, heads, 128] BF16 bits (query prologue input);
+    w_raw:    float32 [tokens, heads] raw head-gate weights;
+    q_codes:  uint8 [tokens, heads, 128] FP8 E4M3 codes and w: float32
+              [tokens, heads] scaled gate weights (logits inputs: random
+              codes, drawn independently of q_bf16);
+    k_fp8:    uint8 [slots, 128] E4M3 codes; k_scale: float32 [slots] > 0;
+    lengths:  int32 [tokens]: token t scores key positions [0, lengths[t]);
+    block_table: int32 [1, pages] shared by the tokens (one request).
+    """
+    name: str
+    q_bf16: np.ndarray
+    w_raw: np.ndarray
+    q_codes: np.ndarray
+    w: np.ndarray
+    k_fp8: np.ndarray
+    k_scale: np.ndarray
+    lengths: np.ndarray
+    block_table: np.ndarray
+    page_size: int
+    positions: np.ndarray
+    cos_sin: np.ndarray
+    rope_dim: int
+    seed: int
+
+    @property
+    def tokens(self) -> int:
+        return int(self.q_codes.shape[0])
+
+    @property
+    def heads(self) -> int:
+        return int(self.q_codes.shape[1])
+
+
+def _e4m3_codes(st: Stream, n: int, lo: int = 0x20, span: int = 0x50) -> np.ndarray:
+    """Random finite E4M3 codes: magnitude codes in [lo, lo + span) (exponents
+    4 to 13 by default, values 2^-3 .. 2^6), random sign. Codes only: no
+    value arithmetic."""
+    mag = (lo + st.below(n, span)).astype(np.uint8)
+    sign = (st.below(n, 2) << 7).astype(np.uint8)
+    return mag | sign
+
+
+def make_logits(tokens: int, keys: int, seed: int = 21, *, heads: int = 64, page_size: int = 64,
+                rope_dim: int = 64, with_table: bool = True) -> LogitsInputs:
+    """`tokens` query tokens of one request (verify: the last `tokens`
+    positions of a context of `keys`), each scoring the causal prefix
+    [0, keys - tokens + 1 + t); keys live in a randomly paged FP8 cache.
+    with_table=False skips the rotary table (only the query prologue reads it)."""
+    st = Stream(seed, 41)
+    d = 128
+    q_bf16 = bf16_bits(st.normal(tokens * heads * d).reshape(tokens, heads, d) * 2.0)
+    w_raw = _f32(st.normal(tokens * heads).reshape(tokens, heads))
+    q_codes = _e4m3_codes(st, tokens * heads * d).reshape(tokens, heads, d)
+    w = _f32(st.normal(tokens * heads).reshape(tokens, heads) * 0.05)
+    pages = (keys + page_size - 1) // page_size
+    pool = pages + 3
+    bt = st.permutation(pool)[:pages][None, :].astype(np.int32)
+    slots = pool * page_size
+    k_fp8 = _e4m3_codes(st, slots * d).reshape(slots, d)
+    k_scale = _f32(0.001 + st.uniform(slots) * 0.01)
+    lengths = (keys - tokens + 1 + np.arange(tokens)).astype(np.int32)
+    positions = (lengths - 1).astype(np.int32)
+    cos_sin = rotary_table(int(keys), rope_dim) if with_table else np.zeros((0, rope_dim), np.float32)
+    return LogitsInputs(f"logits_{tokens}x{keys}", q_bf16, w_raw, q_codes, w, k_fp8, k_scale, lengths, bt,
+                        page_size, positions, cos_sin, rope_dim, seed)
