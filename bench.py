@@ -391,6 +391,79 @@ def sweep_key_prologue(name: str, args) -> bool:
     return parity
 
 
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 matrix peak
+
+
+def sweep_logits(name: str, args) -> bool:
+    """MQA logits of 7 verify tokens x 64 heads over a 1M- or 80K-key paged FP8
+    cache: kernel events, TFLOP/s against the FP8 matrix peak, algorithmic
+    GB/s (key codes and scales read once, FP32 scores written once), and a
+    sampled check against the oracle."""
+    import numpy as np
+    import torch
+    import synth
+    from oracle import indexer_logits as OL
+    from sparse_attention_indexer_amd import logits as G
+    keys = {"logits_7x1m": 1_000_000, "logits_7x80k": 80_000}[name]
+    w = synth.make_logits(7, keys, seed=22, with_table=False)
+    say(f"[bench] sweep {name}: 7 tokens x 64 heads x {keys} keys")
+    dev = torch.device("cuda:0")
+    qc, wq = torch.from_numpy(w.q_codes).to(dev), torch.from_numpy(w.w).to(dev)
+    ks = torch.from_numpy(w.k_scale).to(dev)
+    table = torch.from_numpy(np.ascontiguousarray(w.block_table[0])).to(dev)
+    lengths = torch.from_numpy(w.lengths).to(dev)
+    L_ = int(w.lengths.max())
+    per_copy = w.k_fp8.nbytes
+    ncopy = min(16, max(1, math.ceil(ROTATION_BYTES / per_copy)))
+    kc = [torch.from_numpy(w.k_fp8).to(dev)]
+    kc += [kc[0].clone() for _ in range(ncopy - 1)]
+    out = torch.empty((7, L_), dtype=torch.float32, device=dev)
+
+    def launch(i):
+        G.indexer_mqa_logits(qc, wq, kc[i % ncopy], ks, table, w.page_size, lengths, L_, out)
+
+    for i in range(args.warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        launch(i)
+    torch.cuda.synchronize()
+    wall_us = (time.perf_counter() - t0) / max(1, args.steps) * 1e6
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(max(args.steps, EVENT_STEPS_MIN))]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        launch(i)
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+    got = out.cpu().numpy()
+    ok = True
+    rng = np.random.default_rng(1)
+    for tok in (0, 6):
+        n = int(w.lengths[tok])
+        pos = rng.integers(0, n, 5000)
+        ref, bound = OL.mqa_logits_at(w.q_codes, w.w, w.k_fp8, w.k_scale, w.block_table, 0, w.page_size, tok, pos)
+        ok &= bool(np.all(np.abs(got[tok, pos] - ref) <= 2e-5 * bound + 1e-30))
+    n_scores = int(w.lengths.astype(np.int64).sum())
+    flops = 2 * 128 * 64 * n_scores
+    nbytes = L_ * (128 + 4) + 4 * n_scores + w.q_codes.nbytes + w.w.nbytes + 4 * ((L_ + 63) // 64)
+    p50 = float(np.percentile(t, 50))
+    print(json.dumps({
+        "workload": name, "tokens": 7, "heads": 64, "keys": keys,
+        "kernel_us": {"p50": round(p50, 3), "p10": round(float(np.percentile(t, 10)), 3),
+                      "p90": round(float(np.percentile(t, 90)), 3), "mean": round(float(t.mean()), 3)},
+        "timing": "stream events around each launch (one kernel), 200 launches", "step_us": round(wall_us, 3),
+        "flops": flops, "tflops": round(flops / p50 / 1e6, 1),
+        "frac_of_fp8_peak": round(flops / p50 / 1e6 / PEAK_FP8_TFLOPS, 4),
+        "algorithmic_bytes": nbytes, "gbs": round(nbytes / p50 / 1e3, 1),
+        "frac_of_8tbs": round(nbytes / p50 / 1e3 / PEAK_HBM_GBS, 4),
+        "cache": f"cold key cache ({ncopy} copies)", "parity_sampled": ok, "parity": ok,
+    }), flush=True)
+    return ok
+
+
 def sweep(args) -> int:
     """One JSON line per workload: latency percentiles, rows/s, algorithmic GB/s,
     plan time, parity and the oracle's wall time (1 thread and N threads)."""
@@ -400,6 +473,9 @@ def sweep(args) -> int:
     for name in names:
         if name.startswith("key_prologue"):
             ok &= sweep_key_prologue(name, args)
+            continue
+        if name.startswith("logits_"):
+            ok &= sweep_logits(name, args)
             continue
         w = workload(name)
         say(f"[bench] sweep {name}: {w.rows}x{w.stride}")
@@ -459,7 +535,7 @@ def main() -> int:
                     help="skip the streaming-read ceiling measurement")
     ap.add_argument("--sweep", default="",
                     help="comma list from {c1..c5, c5_g0..c5_g3, cp8_7x125k, prefill_4096x80k, plan_split_600, "
-                         "key_prologue_128k, key_prologue_7}: "
+                         "key_prologue_128k, key_prologue_7, logits_7x1m, logits_7x80k}: "
                          "one JSON line per workload")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))

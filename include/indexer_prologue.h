@@ -96,6 +96,26 @@ topk_status indexer_key_prologue(const indexer_key_config* cfg, const uint16_t* 
                                  const int32_t* block_table, int64_t bt_row_stride, uint8_t* cache_fp8,
                                  float* cache_scale, int64_t num_slots, int32_t* status, void* stream);
 
+/* The fused query path for tokens x heads rows of 128 dims (lmsys page,
+ * section "Indexer Prologue Fusion", query path: RoPE + FP8 quantization +
+ * head-gate scaling). Per (token t, head h):
+ *   y      = rotary of the BF16 row q_act[t][h] at positions[t] (as the key path;
+ *            rope_dim 0 skips it);
+ *   amax   = max |y| floored at 2^-64; codes = E4M3 RNE of y * (448 / amax);
+ *   w_out[t][h] = (w_raw[t][h] * (amax / 448)) * gate_scale  (FP32, in that order):
+ *            the query scale is folded into the head-gate weight, which is
+ *            exact under the indexer's ReLU since the scale is positive.
+ * Layouts: q_act uint16 [tokens][heads][128] and q_codes uint8 [tokens][heads][128]
+ * (16-byte aligned), w_raw / w_out float [tokens][heads], positions int32
+ * [tokens], cos_sin as for the key path (max_pos rows). Errors: bad sizes,
+ * NULLs, alignment, gate_scale <= 0 or not finite -> TOPK_ERR_INVALID_ARG;
+ * a position outside [0, max_pos) (with rope_dim > 0) skips the row and sets
+ * INDEXER_DEVICE_BAD_POSITION in *status (status may be NULL). */
+topk_status indexer_query_prologue(const uint16_t* q_act, int32_t tokens, int32_t heads, const float* w_raw,
+                                   float gate_scale, const float* cos_sin, int32_t rope_dim, int32_t max_pos,
+                                   const int32_t* positions, uint8_t* q_codes, float* w_out, int32_t* status,
+                                   void* stream);
+
 /* Test hook: the kernel's own FP32 -> E4M3 conversion (saturating, round to
  * nearest even) of n values, x[i] -> out[i]. Passage: none (a window on the
  * quantizer of indexer_key_prologue). */

@@ -128,3 +128,19 @@ def error_bound(q_codes, w, k_cache_fp8, k_cache_scale, block_table, bt_row_stri
         ka = np.abs(P.e4m3_decode(k_cache_fp8[slots]))
         out[t, :n] = k_cache_scale[slots] * (np.abs(np.asarray(w[t], np.float64)) @ (qa[t] @ ka.T))
     return out
+
+
+def mqa_logits_at(q_codes, w, k_cache_fp8, k_cache_scale, block_table, bt_row_stride: int, page_size: int,
+                  t: int, positions, row: int = 0):
+    """The scores of query token t at the given key positions only (the same
+    formula as mqa_logits, for spot checks of long rows), and their error-bound
+    magnitudes (as error_bound). Returns (scores float64, bound float64)."""
+    pos = np.asarray(positions, dtype=np.int64)
+    slots = P.slots_of(pos, np.full(pos.shape, row), block_table, bt_row_stride, page_size)
+    qd = P.e4m3_decode(q_codes[t])                      # [H, D]
+    kd = P.e4m3_decode(k_cache_fp8[slots])              # [n, D]
+    ks = k_cache_scale[slots].astype(np.float64)
+    w64 = np.asarray(w[t], np.float64)
+    scores = ks * (w64 @ np.maximum(qd @ kd.T, 0.0))
+    bound = ks * (np.abs(w64) @ (np.abs(qd) @ np.abs(kd).T))
+    return scores, bound

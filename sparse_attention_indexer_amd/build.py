@@ -1,7 +1,7 @@
 """Build the HIP library ``libsparse_topk.so`` in-tree for gfx950.
 
 Usage: ``python -m sparse_attention_indexer_amd.build`` (or ``build()``).
-hipcc cross-compiles without a GPU present. The two sources compile to
+hipcc cross-compiles without a GPU present. The sources compile to
 objects in ``_build/`` side by side, then link into the shared library.
 
 ``build_api_sanitizer_driver()`` builds ``_build/api_asan_driver``: the C ABI
@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsparse_topk.so")
-SOURCES = ["topk_kernels.hip", "topk_api.hip", "prologue.hip"]
+SOURCES = ["topk_kernels.hip", "topk_api.hip", "prologue.hip", "logits.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ROCM_LIB = "/opt/rocm/lib"
 CLANGXX = "/opt/rocm/llvm/bin/clang++"   # host compiler of hipcc: one sanitizer runtime for all objects

@@ -186,6 +186,72 @@ __global__ void __launch_bounds__(kPrologueBlock) key_prologue_kernel(KeyArgs a)
     if (live[u]) key_token(a, sub, pos[u], page[u], raw[u], w, bb, c[u], s[u]);
 }
 
+// Query path: rotary, per-(token, head) FP8 E4M3 and the head-gate weight
+// with the query scale folded in. Same lane layout as the key path: 16 lanes
+// per (token, head) row of 128 dims.
+struct QueryArgs {
+  const uint16_t* q;        // [T][H][128] BF16 bits
+  int32_t rows;             // T * H
+  int32_t heads;
+  const float* w_raw;       // [T][H]
+  float gate_scale;
+  const float* cos_sin;
+  int32_t rope_dim;
+  int32_t max_pos;
+  const int32_t* positions; // [T]
+  uint8_t* q_codes;         // [T][H][128]
+  float* w_out;             // [T][H]
+  int32_t* status;
+};
+
+__global__ void __launch_bounds__(kPrologueBlock) query_prologue_kernel(QueryArgs a) {
+  const int sub = (int)(threadIdx.x & (kLanesPerToken - 1));
+  const int64_t r = (int64_t)blockIdx.x * kGroupsPerBlock + (threadIdx.x / kLanesPerToken);
+  if (r >= a.rows) return;   // (uniform over the row's 16 lanes)
+  const int32_t pos = a.positions[r / a.heads];
+  const bool rot = sub * kDimsPerLane < a.rope_dim;
+  if (a.rope_dim > 0 && (pos < 0 || pos >= a.max_pos)) {
+    if (sub == 0 && a.status) atomicOr(a.status, INDEXER_DEVICE_BAD_POSITION);
+    return;
+  }
+  const uint4 raw = *reinterpret_cast<const uint4*>(a.q + r * kKeyDim + sub * kDimsPerLane);
+  float4 c = make_float4(1.f, 1.f, 1.f, 1.f), s = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (rot) {
+    const float* cs = a.cos_sin + (int64_t)pos * a.rope_dim + sub * (kDimsPerLane / 2);
+    c = *reinterpret_cast<const float4*>(cs);
+    s = *reinterpret_cast<const float4*>(cs + a.rope_dim / 2);
+  }
+  const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
+  float y[kDimsPerLane];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    y[2 * i] = __uint_as_float(words[i] << 16);
+    y[2 * i + 1] = __uint_as_float(words[i] & 0xFFFF0000u);
+  }
+  const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float p = y[2 * i], q = y[2 * i + 1];
+    y[2 * i] = p * cc[i] - q * ss[i];
+    y[2 * i + 1] = p * ss[i] + q * cc[i];
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < kDimsPerLane; ++i) m = fmaxf(m, fabsf(y[i]));
+  const float amax = fmaxf(group_max(m), kAmaxFloor);
+  const float inv = kE4M3Max / amax;
+  int lo = 0, hi = 0;
+  lo = cvt2_e4m3<false>(y[0] * inv, y[1] * inv, lo);
+  lo = cvt2_e4m3<true>(y[2] * inv, y[3] * inv, lo);
+  hi = cvt2_e4m3<false>(y[4] * inv, y[5] * inv, hi);
+  hi = cvt2_e4m3<true>(y[6] * inv, y[7] * inv, hi);
+  *reinterpret_cast<uint2*>(a.q_codes + r * kKeyDim + sub * kDimsPerLane) = make_uint2((uint32_t)lo, (uint32_t)hi);
+  if (sub == 0) {
+    const float q_scale = amax / kE4M3Max;
+    a.w_out[r] = (a.w_raw[r] * q_scale) * a.gate_scale;
+  }
+}
+
 __global__ void debug_fp8_kernel(const float* x, int64_t n, uint8_t* out) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     out[i] = (uint8_t)(cvt2_e4m3<false>(x[i], 0.f, 0) & 0xFF);
@@ -240,6 +306,36 @@ topk_status indexer_key_prologue(const indexer_key_config* cfg, const uint16_t* 
   const unsigned blocks = (unsigned)((num_tokens + kTokensPerBlock - 1) / kTokensPerBlock);
   hipLaunchKernelGGL(key_prologue_kernel, dim3(blocks), dim3(kPrologueBlock), 0,
                      static_cast<hipStream_t>(stream), a);
+  return hipGetLastError() == hipSuccess ? TOPK_OK : TOPK_ERR_HIP;
+}
+
+topk_status indexer_query_prologue(const uint16_t* q_act, int32_t tokens, int32_t heads, const float* w_raw,
+                                   float gate_scale, const float* cos_sin, int32_t rope_dim, int32_t max_pos,
+                                   const int32_t* positions, uint8_t* q_codes, float* w_out, int32_t* status,
+                                   void* stream) {
+  if (tokens < 0 || heads < 1 || rope_dim < 0 || rope_dim > kKeyDim || rope_dim % 8 != 0 || max_pos < 1 ||
+      !(gate_scale > 0.f) || !(gate_scale < 3.0e38f) || (int64_t)tokens * heads > 0x7FFFFFFF)
+    return TOPK_ERR_INVALID_ARG;
+  if (tokens == 0) return TOPK_OK;
+  if (!q_act || !w_raw || !positions || !q_codes || !w_out || (rope_dim > 0 && !cos_sin)) return TOPK_ERR_INVALID_ARG;
+  auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; };
+  if (misaligned(q_act) || misaligned(q_codes) || (rope_dim > 0 && misaligned(cos_sin))) return TOPK_ERR_INVALID_ARG;
+  QueryArgs a;
+  a.q = q_act;
+  a.rows = tokens * heads;
+  a.heads = heads;
+  a.w_raw = w_raw;
+  a.gate_scale = gate_scale;
+  a.cos_sin = cos_sin;
+  a.rope_dim = rope_dim;
+  a.max_pos = max_pos;
+  a.positions = positions;
+  a.q_codes = q_codes;
+  a.w_out = w_out;
+  a.status = status;
+  const unsigned blocks = (unsigned)((a.rows + kGroupsPerBlock - 1) / kGroupsPerBlock);
+  hipLaunchKernelGGL(query_prologue_kernel, dim3(blocks), dim3(kPrologueBlock), 0, static_cast<hipStream_t>(stream),
+                     a);
   return hipGetLastError() == hipSuccess ? TOPK_OK : TOPK_ERR_HIP;
 }
 

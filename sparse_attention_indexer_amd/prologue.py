@@ -37,6 +37,8 @@ def _lib():
         lib.indexer_key_prologue.restype = ctypes.c_int
         lib.indexer_debug_fp8.argtypes = [V, I64, V, V]
         lib.indexer_debug_fp8.restype = ctypes.c_int
+        lib.indexer_query_prologue.argtypes = [V, I32, I32, V, ctypes.c_float, V, I32, I32, V, V, V, V, V]
+        lib.indexer_query_prologue.restype = ctypes.c_int
         _bound = True
     return lib
 
@@ -96,6 +98,39 @@ def indexer_key_prologue(k_act: torch.Tensor, ln_weight: torch.Tensor, ln_bias: 
         cache_fp8.data_ptr(), cache_scale.data_ptr(), cache_fp8.shape[0],
         None if status is None else status.data_ptr(), topk._stream(stream))
     topk._check("indexer_key_prologue", st)
+
+
+def indexer_query_prologue(q_act: torch.Tensor, w_raw: torch.Tensor, gate_scale: float,
+                           cos_sin: torch.Tensor | None, rope_dim: int, positions: torch.Tensor,
+                           status: torch.Tensor | None = None, stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Enqueue the fused query path; returns (q_codes uint8 [T, H, 128], w_out
+    float32 [T, H]) allocated here by torch (the library itself allocates nothing).
+
+    q_act: bfloat16 or int16/uint16 bits [T, H, 128], contiguous; w_raw float32 [T, H]."""
+    _need(q_act, (torch.bfloat16, torch.int16, torch.uint16), "q_act")
+    _need(w_raw, (torch.float32,), "w_raw")
+    _need(positions, (torch.int32,), "positions")
+    if q_act.dim() != 3 or q_act.shape[2] != KEY_DIM or not q_act.is_contiguous():
+        raise ValueError("q_act must be a contiguous [tokens, heads, 128] tensor")
+    T, H = q_act.shape[0], q_act.shape[1]
+    if tuple(w_raw.shape) != (T, H) or not w_raw.is_contiguous() or positions.numel() != T:
+        raise ValueError("w_raw must be [tokens, heads] and positions [tokens]")
+    max_pos = 2 ** 31 - 1
+    if rope_dim:
+        if cos_sin is None:
+            raise ValueError("rope_dim > 0 needs cos_sin")
+        _need(cos_sin, (torch.float32,), "cos_sin")
+        if not cos_sin.is_contiguous() or cos_sin.dim() != 2 or cos_sin.shape[1] != rope_dim:
+            raise ValueError("cos_sin must be a contiguous [max_pos, rope_dim] table")
+        max_pos = cos_sin.shape[0]
+    codes = torch.empty((T, H, KEY_DIM), dtype=torch.uint8, device=q_act.device)
+    w_out = torch.empty((T, H), dtype=torch.float32, device=q_act.device)
+    st = _lib().indexer_query_prologue(q_act.data_ptr(), T, H, w_raw.data_ptr(), float(gate_scale),
+                                       None if cos_sin is None else cos_sin.data_ptr(), int(rope_dim), int(max_pos),
+                                       positions.data_ptr(), codes.data_ptr(), w_out.data_ptr(),
+                                       None if status is None else status.data_ptr(), topk._stream(stream))
+    topk._check("indexer_query_prologue", st)
+    return codes, w_out
 
 
 def debug_fp8(x: torch.Tensor, stream=None) -> torch.Tensor:

@@ -151,3 +151,13 @@ def test_planted_logits_mistakes(monkeypatch, fn):
 
 def test_pins_accept_real_logits_oracle():
     assert _pins_pass()
+
+
+def test_logits_at_positions_is_the_row_restricted():
+    q, w, k, ks, table, ps, lengths = _case(T=2)
+    full = L.mqa_logits(q, w, k, ks, table, 0, ps, lengths)
+    bound = L.error_bound(q, w, k, ks, table, 0, ps, lengths)
+    pos = np.array([0, 3, 17, int(lengths[1]) - 1])
+    for t in range(2):
+        s, b = L.mqa_logits_at(q, w, k, ks, table, 0, ps, t, pos)
+        assert np.allclose(s, full[t, pos], rtol=1e-14) and np.allclose(b, bound[t, pos], rtol=1e-14)
