@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsparse_topk.so")
-SOURCES = ["topk_kernels.hip", "topk_api.hip", "prologue.hip", "logits.hip"]
+SOURCES = ["topk_kernels.hip", "topk_api.hip", "prologue.hip", "logits.hip", "hisparse.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ROCM_LIB = "/opt/rocm/lib"
 CLANGXX = "/opt/rocm/llvm/bin/clang++"   # host compiler of hipcc: one sanitizer runtime for all objects

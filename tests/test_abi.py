@@ -19,7 +19,7 @@ def declared_functions():
     names = set()
     for h in HEADERS:
         src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
-        names |= set(re.findall(r"\b((?:topk|indexer)_[a-z0-9_]+)\s*\(", src))
+        names |= set(re.findall(r"\b((?:topk|indexer|hisparse)_[a-z0-9_]+)\s*\(", src))
     return sorted(names)
 
 
@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
     for n in ("topk_query_sizes", "topk_plan", "topk_select_paged", "topk_workspace_init",
               "topk_read_status", "topk_status_string", "topk_register_capacity", "topk_debug_keys",
               "topk_debug_stream_read", "topk_stream_read_groups",
-              "topk_select_paged_timed", "topk_debug_histogram", "indexer_key_prologue", "indexer_debug_fp8"):
+              "topk_select_paged_timed", "topk_debug_histogram", "indexer_key_prologue", "indexer_debug_fp8", "indexer_query_prologue", "indexer_mqa_logits",
+              "hisparse_resolve"):
         assert n in names
 
 
