@@ -98,7 +98,8 @@ topk_status sizing(const topk_config* cfg, Sizing* s) {
   if (cfg->wg_per_row > per_row) per_row = cfg->wg_per_row;
   if (per_row < 1) per_row = 1;
   const int64_t want = (int64_t)cfg->max_rows * per_row;
-  const int64_t cap = (int64_t)d.cus * d.per_cu;
+  int64_t cap = (int64_t)d.cus * d.per_cu;
+  if (cap > kMaxRowGroups) cap = kMaxRowGroups;   // (a split row's vote counts its workgroups in 9 bits)
   s->grid = (int)(want < cap ? want : cap);
   s->max_items = s->grid + cfg->max_rows;
   int groups = s->grid / 2;

@@ -258,6 +258,12 @@ constexpr int kStageCap = kListCap - kPreCap / 2;  // staged candidates below th
 // above at most kFineListOff staged candidates and below the position list.
 constexpr int kFineListOff = 8192;
 static_assert(kFineListOff + kFineBins / 2 <= kStageCap, "fine-digit counters below the position list");
+// A workgroup that classifies its chunk before the row's histogram is merged
+// (a predicted crowded threshold bin, see split_row) stages its outputs above
+// that bin (positions, then block-table entries) here, clear of the merged
+// histogram it is about to read into rhist and of the prefixes in outpos.
+constexpr int kSpecStageOff = kFineListOff + kFineBins / 2;
+static_assert(kSpecStageOff + kMaxK <= kStageCap, "predicted-bin outputs below the position list");
 static_assert(kWideWords * 4 <= kListCap * 8, "first-digit histogram aliases the LDS list");
 static_assert(kMaxK <= kRadixBins, "above-threshold staging aliases rhist");
 
@@ -1414,6 +1420,40 @@ constexpr uint32_t kFineHistEntry = kFineMaxCand;             // ... then the di
 static_assert(kFineHistEntry + kFineBins / 2 <= (uint32_t)kListCap, "candidates and digit counts share the LDS list");
 static_assert(kFineMaxCand % kLdsCopyWords == 0, "the rounded-up copy stays below the digit counts");
 
+// A workgroup's fine-digit counts in LDS go to the row's digit histogram, one
+// atomic per nonzero digit; once this wave's atomics have landed (its own
+// wait), the digit groups' sums go to the row's coarse counts. A reader that
+// finds the coarse counts complete therefore also reads a complete digit
+// histogram, and polls 128 words instead of 8,192. Wave w takes digits
+// 512 j + 64 w + lane: one instruction adds a whole group of 64 consecutive
+// digits, which the memory system merges per cache line (one digit per
+// instruction, hot digits shared by every workgroup of the row serialise
+// there instead), and the group's sum is a wave sum.
+static_assert(kFineBins == 16 * kBlock && kFineGroups * 64 == kFineBins, "16 digit groups per wave");
+__device__ __forceinline__ void merge_fine(const uint32_t* lfine, GroupState* g) {
+  const int t = threadIdx.x;
+  const uint32_t w = uni((uint32_t)t >> 6);
+  uint32_t sum = 0;   // lane j holds the sum of the wave's group j
+#pragma unroll 1
+  for (int j = 0; j < kFineBins / kBlock; ++j) {
+    const int d = j * kBlock + t;
+    const uint32_t c = lfine[d];
+    if (c) __hip_atomic_fetch_add(&g->fine[d], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t s = wave_sum_u32(c);
+    sum = lane() == (uint32_t)j ? s : sum;
+  }
+  drain_memory();
+  if (sum)   // (lanes below 16 only)
+    __hip_atomic_fetch_add(&g->fine_c[lane() * kWaves + w], sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// How a workgroup's fine-digit counts reach the row (fine_tail):
+enum FineMerge {
+  kFineMerged = 0,   // already merged (classified before the histogram wait)
+  kFineInLds = 1,    // digit counts in LDS at kFineListOff
+  kFineGlobal = 2,   // digits added to the row's histogram directly, group sums in LDS (lhist)
+};
+
 // Every workgroup of a split row whose threshold bin holds more than
 // kFineMin candidates ("fine" rows), after classifying its chunk: its
 // candidates sit in the LDS list as fine-frame composite keys (fine_key_frame)
@@ -1430,41 +1470,29 @@ static_assert(kFineMaxCand % kLdsCopyWords == 0, "the rounded-up copy stays belo
 template <bool VEC>
 __device__ __forceinline__ void fine_tail(const SelectArgs& a, GroupState* g, uint64_t* slab, int32_t len,
                                           uint32_t G, uint32_t k, uint32_t n_above, uint32_t cnt,
-                                          uint32_t local_above, bool fine_lds, Refine p, Smem& sh,
-                                          const RowOut& o, bool bad) {
+                                          uint32_t local_above, int merge, Refine p, Smem& sh,
+                                          const RowOut& o, bool bad, uint32_t* staged, uint32_t* staged_pg,
+                                          uint32_t surv_cap) {
   const int t = threadIdx.x;
   const uint32_t w = uni((uint32_t)t >> 6);
   const uint32_t need = k - n_above;
   const uint32_t* lfine = reinterpret_cast<const uint32_t*>(sh.list + kFineListOff);
+  if (merge == kFineGlobal) drain_memory();   // (this wave's digit atomics land before the group sums go)
   __syncthreads();   // classification complete (staged list, digit counts, above-threshold outputs)
-  if (fine_lds) {
-    for (int i = t; i < kFineBins; i += kBlock) {
-      const uint32_t c = lfine[i];
-      if (c) __hip_atomic_fetch_add(&g->fine[i], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+  if (merge == kFineInLds) merge_fine(lfine, g);
+  if (merge == kFineGlobal && t < kFineGroups && sh.lhist[t])
+    __hip_atomic_fetch_add(&g->fine_c[t], sh.lhist[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // Poll the coarse counts (lane t < 128 holds group 127 - t: thread order
+  // runs from the top group down) until they add up to the threshold bin's
+  // total: every contribution only adds, so a read that reaches the total
+  // has read every final count (the snapshot argument of the first wait),
+  // and every digit behind them has landed.
   bool ok = false;
-  // Lane t holds digits 8191 - 16 t down to 8176 - 16 t (lanes in thread order
-  // cover the digits from the top down), read as 8 word pairs.
-  constexpr int kPer = kFineBins / kBlock;
-  static_assert(kPer == 16, "16 digits per lane");
-  const uint32_t top = (uint32_t)(kFineBins - kPer * t) - 1u;
-  const uint64_t* fp = reinterpret_cast<const uint64_t*>(g->fine) + (top - (kPer - 1)) / 2;
-  uint32_t hv[kPer];
-  uint32_t s = 0, cum = 0;
+  uint32_t gc = 0, gcum = 0;
   for (uint32_t spins = 0; spins < a.spin_limit; ++spins) {
-    uint64_t q[kPer / 2];
-#pragma unroll
-    for (int i = 0; i < kPer / 2; ++i) q[i] = ld_agent(fp + i);
-    s = 0;
-#pragma unroll
-    for (int i = 0; i < kPer / 2; ++i) {
-      hv[2 * i] = (uint32_t)q[i];
-      hv[2 * i + 1] = (uint32_t)(q[i] >> 32);
-      s += hv[2 * i] + hv[2 * i + 1];
-    }
+    gc = t < kFineGroups ? ld_agent(&g->fine_c[kFineGroups - 1 - t]) : 0u;
     uint32_t tot;
-    cum = block_exclusive_add(s, sh.scratch, &tot);   // candidates in the digits above this lane's
+    gcum = block_exclusive_add(gc, sh.scratch, &tot);   // candidates in the groups above this lane's
     if (uni(tot) == cnt) {
       ok = true;
       break;
@@ -1475,28 +1503,28 @@ __device__ __forceinline__ void fine_tail(const SelectArgs& a, GroupState* g, ui
     if (t == 0) atomicOr(a.status, TOPK_DEVICE_SPIN_TIMEOUT);
     return;
   }
-  if (t == 0) sh.res[0] = kNotFound;
+  if (t == 0) sh.res[0] = sh.res[2] = kNotFound;
   __syncthreads();
-  if (cum < need && need <= cum + s) {
-    // (selects, one store: a store per digit would hold 16 value triples;
-    // the digit's index i among the lane's 16, not the digit itself: per-i
-    // digit values are loop-invariant and would be hoisted into registers)
-    uint32_t c = cum, fi = 0, fc = 0, fh = 0;
-#pragma unroll
-    for (int i = kPer - 1; i >= 0; --i) {   // from digit top down
-      const uint32_t h = hv[i];
-      const bool hit = c < need && need <= c + h;
-      fi = hit ? (uint32_t)i : fi;
-      fc = hit ? c : fc;
-      fh = hit ? h : fh;
-      c += h;
-    }
-    sh.res[0] = top - (uint32_t)(kPer - 1) + fi;
-    sh.res[1] = fc;
-    sh.res[2] = fh;
+  if (t < kFineGroups && gcum < need && need <= gcum + gc) {
+    sh.res[0] = (uint32_t)(kFineGroups - 1 - t);
+    sh.res[1] = gcum;
   }
   __syncthreads();
-  const uint32_t dstar = uni(sh.res[0]), above = uni(sh.res[1]), cnt_d = uni(sh.res[2]);
+  // The group holding the need-th candidate: one wave reads its 64 digits,
+  // top first, and finds d* with a wave prefix sum.
+  const uint32_t grp = uni(sh.res[0]);
+  if (grp != kNotFound && t < kWave) {
+    const uint32_t d = grp * 64u + 63u - (uint32_t)t;
+    const uint32_t h = ld_agent(&g->fine[d]);
+    const uint32_t c = uni(sh.res[1]) + wave_inclusive_add(h) - h;
+    if (c < need && need <= c + h) {
+      sh.res[2] = d;
+      sh.res[3] = c;
+      sh.bcast[3] = h;
+    }
+  }
+  __syncthreads();
+  const uint32_t dstar = uni(sh.res[2]), above = uni(sh.res[3]), cnt_d = uni(sh.bcast[3]);
   const bool found = dstar != kNotFound;
   const bool all_of_d = found && cnt_d == need - above;
   const uint32_t dsel = all_of_d ? dstar : dstar + 1u;
@@ -1545,11 +1573,9 @@ __device__ __forceinline__ void fine_tail(const SelectArgs& a, GroupState* g, ui
   // not fit there, stored to the row's list once the reservation returns.
   const uint32_t surv_off = (n_c + 1u) & ~1u;
   const bool room = n_above_loc + tsel <= (uint32_t)kMaxK;
-  const bool stage_surv = surv_off + tkeep <= (uint32_t)kStageCap;
+  const bool stage_surv = surv_off + tkeep <= surv_cap;
   if (!stage_surv) __syncthreads();
   const uint32_t bc_direct = stage_surv ? 0u : uni(sh.bcast[1]);
-  uint32_t* staged = sh.rhist;
-  uint32_t* staged_pg = sh.outpos;
   if (room) {
     uint32_t ao = n_above_loc + bsel, ko = bkeep;
     for (uint32_t i0 = lo; i0 < hi; i0 += kWave) {
@@ -1614,10 +1640,12 @@ __device__ __forceinline__ void fine_tail(const SelectArgs& a, GroupState* g, ui
   if (!found && t == 0) atomicOr(a.status, TOPK_DEVICE_INTERNAL);
   uint64_t* fg = reinterpret_cast<uint64_t*>(g->fine);
   for (int i = t; i < kFineBins / 2; i += kBlock) st_agent(fg + i, (uint64_t)0);
+  if (t < kFineGroups) st_agent(&g->fine_c[t], 0u);
   for (int r = t; r < kBins; r += kBlock) st_agent(&g->hist[r], 0u);
   if (t < 4) st_agent(&g->range[t], 0u);
   if (t == 0) {
-    st_agent(&g->arrive, 0u);
+    st_agent(&g->arrive, (uint64_t)0);
+    st_agent(&g->vsq, (uint64_t)0);
     st_agent(&g->emit, 0u);
     st_agent(&g->cand, 0u);
     st_agent(&g->done, 0u);
@@ -1660,7 +1688,10 @@ __device__ __forceinline__ void resolve_split(const SelectArgs& a, GroupState* g
 }
 
 // A row shared by w.gsize workgroups; this one holds chunk [w.begin, end).
-template <bool VEC>
+// EARLY: the predicted-bin vote and early classification are compiled in
+// (the variant for tile-sized chunks; elsewhere the code would only cost
+// instruction-cache room).
+template <bool VEC, bool EARLY>
 __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w, int32_t len, const float* rowp,
                                           const RowOut& o, bool resident, uint32_t (&hk)[kHk], Smem& sh) {
   const int t = threadIdx.x;
@@ -1681,7 +1712,8 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
   // The scores of the chunk that no merged bin counts go to g->arrive, so the
   // merged bins and that count add up to the row length once every
   // workgroup's atomics have landed: there is no separate arrival (and no
-  // wait for the atomics before it).
+  // wait for the atomics before it). The vote below rides on the same
+  // check.
   uint32_t merged = 0;
   for (int r = t; r < kBins; r += kBlock) {
     const uint32_t h = sh.lhist[r];
@@ -1695,14 +1727,31 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
   // While the other workgroups merge: list the positions at or above the
   // local T-th bin and start reading their scores and block-table entries.
   uint32_t* pre = reinterpret_cast<uint32_t*>(sh.list + kStageCap);
+  uint32_t* lfine = reinterpret_cast<uint32_t*>(sh.list + kFineListOff);
   float pv[kPreRegs];
   int32_t ppg[kPreRegs];
   uint32_t n_pre = 0xFFFFFFFFu, bpre = kNotFound;
+  // A predicted crowded threshold bin. A chunk whose T-th bin holds many
+  // scores while few lie above it expects the row's threshold bin there: it
+  // proposes that bin, classifies its pre-read scores against it while the
+  // histograms merge, and adds their fine-digit counts to the row early.
+  // Every workgroup votes (proposers with v = bin + 1, the others with 0):
+  // the proposer count and the sum of v go to the high half of the rest
+  // count's word, the sum of v^2 to a word whose low half counts the
+  // workgroups, each in one atomic with a part of the completeness check, so
+  // the merged histogram's snapshot also holds every vote. The early counts are used only if every proposal
+  // equals the row's threshold bin: the count n, the sum and the sum of
+  // squares of the proposals then read n, n (b* + 1) and n (b* + 1)^2, which
+  // no other set of n proposals gives (see `fine` below).
+  bool propose = false;
+  uint32_t vote = 0u;
   if (!resident) {
     uint32_t tot_merged;
     block_exclusive_add(merged, sh.scratch, &tot_merged);
-    if (t == 0)
-      __hip_atomic_fetch_add(&g->arrive, chunk - tot_merged, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t == 0) {
+      __hip_atomic_fetch_add(&g->arrive, (uint64_t)(chunk - tot_merged), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if constexpr (EARLY) __hip_atomic_fetch_add(&g->vsq, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   } else {
     bpre = uni(sh.res[3]);
     const uint64_t pm = interest_mask(hk, cut_of_bin(bpre).vlo);
@@ -1714,8 +1763,27 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
     uint32_t off = block_exclusive_add((merged << 16) | (uint32_t)__popcll(pm), sh.scratch, &tot);
     off &= 0xFFFFu;
     n_pre = uni(tot) & 0xFFFFu;
-    if (t == 0)
-      __hip_atomic_fetch_add(&g->arrive, chunk - (uni(tot) >> 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // (every score at or above bpre is pre-read, the bin's candidates fit the
+    // LDS list below the digit counters, and fewer than k / G lie above it)
+    if constexpr (EARLY) {
+      const uint32_t lc = uni(sh.lhist[raw_of_bin(bpre)]);
+      propose = n_pre <= (uint32_t)kPreCap && lc <= (uint32_t)kFineListOff && lc * G > kFineMin &&
+                count_above(sh.lhist, cum, bpre) * G < k;
+      vote = propose ? bpre + 1u : 0u;
+    }
+    if (t == 0) {
+      __hip_atomic_fetch_add(&g->arrive,
+                             (uint64_t)(chunk - (uni(tot) >> 16)) | ((uint64_t)((uint32_t)propose | (vote << 9)) << 32),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if constexpr (EARLY) {
+        __hip_atomic_fetch_add(&g->vsq, (uint64_t)1 | ((uint64_t)(vote * vote) << 32), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        sh.cur_out = 0;
+        sh.cur_list = 0;
+      }
+    }
+    if (propose)
+      for (int i = t; i < kFineBins / 4; i += kBlock) reinterpret_cast<uint4*>(lfine)[i] = make_uint4(0u, 0u, 0u, 0u);
     if (n_pre <= (uint32_t)kPreCap) {
       uint64_t m = pm;
       while (m) {
@@ -1735,6 +1803,41 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
       }
     }
   }
+  bool spec_bad = false;
+  uint32_t* sstaged = reinterpret_cast<uint32_t*>(sh.list + kSpecStageOff);
+  uint32_t* sstaged_pg = sstaged + kMaxK;
+  if (EARLY && propose) {
+    const Cut scut = cut_of_bin(bpre);
+    const Refine sf = fine_key_frame(fine_frame(bpre), (uint32_t)len);
+    const uint32_t sshift = sf.nb - (uint32_t)kFineBits;
+    Range srg;
+#pragma unroll
+    for (int i = 0; i < kPreRegs; ++i) {
+      const uint32_t idx = (uint32_t)(t + i * kBlock);
+      if (idx < n_pre)
+        classify(
+            pv[i], (int32_t)pre[idx], ppg[i], scut, srg,
+            [&](int32_t e, int32_t pg) {
+              const uint32_t c = atomicAdd(&sh.cur_out, 1u);
+              const bool ok = c < (uint32_t)kMaxK;
+              if (ok) {
+                sstaged[c] = (uint32_t)e;
+                sstaged_pg[c] = (uint32_t)pg;
+              }
+              spec_bad |= !ok;
+            },
+            [&](uint32_t kk, int32_t e) {
+              const uint64_t v = sf.key(kk, e);
+              atomicAdd(&lfine[min((uint32_t)(v >> sshift), (uint32_t)kFineBins - 1u)], 1u);
+              const uint32_t c = atomicAdd(&sh.cur_list, 1u);
+              const bool ok = c < (uint32_t)kFineListOff;
+              if (ok) sh.list[c] = v;
+              spec_bad |= !ok;
+            });
+    }
+    __syncthreads();
+    merge_fine(lfine, g);
+  }
   // Read the merged bins and the rest count until they add up to the row
   // length. Every contribution is a non-negative add, so each value read is
   // at most its final value; a read that sums to the final total therefore
@@ -1743,14 +1846,16 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
     static_assert(kBins == 2 * kBlock, "two bins per lane");
     // At most spin_limit polls (uniform); a limit of 0 gives up at once.
     bool ok = false;
+    static_assert(offsetof(GroupState, vsq) == offsetof(GroupState, arrive) + 128, "vote word one line past arrive");
     for (uint32_t spins = 0; spins < a.spin_limit; ++spins) {
       const uint32_t h0 = ld_agent(&g->hist[t]), h1 = ld_agent(&g->hist[t + kBlock]);
-      const uint32_t rest = t == 0 ? ld_agent(&g->arrive) : 0u;
+      const uint64_t v = t < (EARLY ? 2 : 1) ? ld_agent(&g->arrive + 16 * t) : (uint64_t)0;
       sh.rhist[t] = h0;
       sh.rhist[t + kBlock] = h1;
+      if (t < 2) sh.pl_red2[t] = (uint32_t)(v >> 32);
       uint32_t tot;
-      block_exclusive_add(h0 + h1 + rest, sh.scratch, &tot);
-      if (uni(tot) == (uint32_t)len) {
+      block_exclusive_add(h0 + h1 + (uint32_t)v, sh.scratch, &tot);
+      if (uni(tot) == (uint32_t)len + (EARLY ? G : 0u)) {   // (the rest count, then one per workgroup)
         ok = true;
         break;
       }
@@ -1780,14 +1885,19 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
   // A large threshold bin (uniform across the row's workgroups): its
   // candidates are also counted by fine digit, in LDS when the staged list
   // leaves room for the counters, else straight into the row's global digit
-  // histogram.
-  const bool fine = keep && cnt > kFineMin && cnt <= kFineMaxCand;
+  // histogram. With a predicted bin, only if the prediction holds: the
+  // digit histogram then already holds the early counts, and the workgroups
+  // that made them skip their classification (pre_done); a wrong prediction
+  // leaves stray counts, so the row takes the path without digit counts.
+  const uint32_t n_prop = EARLY ? uni(sh.pl_red2[0]) & 511u : 0u;
+  const uint64_t b1 = (uint64_t)bstar + 1u;
+  const bool agree = !EARLY || ((uint64_t)(uni(sh.pl_red2[0]) >> 9) == n_prop * b1 &&
+                                (uint64_t)uni(sh.pl_red2[1]) == n_prop * b1 * b1);
+  const bool fine = keep && cnt > kFineMin && cnt <= kFineMaxCand && agree;   // (n_prop = 0 agrees)
+  const bool pre_done = EARLY && propose && fine;   // (then this workgroup's proposal is b*)
   const bool fine_lds = local_cnt <= (uint32_t)kFineListOff;
   const Refine pf = fine_key_frame(fine_frame(bstar), (uint32_t)len);
   const uint32_t dshift = pf.nb - (uint32_t)kFineBits;
-  uint32_t* lfine = reinterpret_cast<uint32_t*>(sh.list + kFineListOff);
-  if (fine && fine_lds)   // (ordered before the counting by the barrier below)
-    for (int i = t; i < kFineBins / 4; i += kBlock) reinterpret_cast<uint4*>(lfine)[i] = make_uint4(0u, 0u, 0u, 0u);
   // This workgroup's output and candidate offsets in the row; their round
   // trips overlap the re-reads of the extraction below.
   // Thread 0 uses the atomics' results only after the extraction (nothing
@@ -1795,7 +1905,7 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
   // for the round trip); only the rare unstaged case, candidates written
   // straight to global memory, needs its base first.
   uint32_t base_out = 0, base_cand = 0;
-  if (t == 0) {
+  if (t == 0 && !pre_done) {
     sh.cur_out = 0;
     sh.cur_list = 0;
     sh.range[0] = sh.range[1] = sh.range[2] = sh.range[3] = 0;
@@ -1809,6 +1919,13 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
       base_cand = __hip_atomic_fetch_add(&g->cand + z, local_cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
+  if (fine && !pre_done) {   // digit counters (every wave has read its local bins above)
+    if (fine_lds)
+      for (int i = t; i < kFineBins / 4; i += kBlock) reinterpret_cast<uint4*>(lfine)[i] = make_uint4(0u, 0u, 0u, 0u);
+    else if (t < kFineGroups)
+      sh.lhist[t] = 0u;
+    __syncthreads();
+  }
   if (keep && !stage) {
     if (t == 0) sh.cur_list = base_cand;
     __syncthreads();
@@ -1839,6 +1956,7 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
         atomicAdd(&lfine[d], 1u);
       } else {
         __hip_atomic_fetch_add(&g->fine[d], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        atomicAdd(&sh.lhist[d >> 6], 1u);
       }
     }
     const uint32_t c = atomicAdd(&sh.cur_list, 1u);
@@ -1847,7 +1965,7 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
     if (ok && !stage) st_agent(slab + c, v);
     bad |= !ok;
   };
-  if (found) {
+  if (found && !pre_done) {
     if (resident && n_pre <= (uint32_t)kPreCap && bstar >= bpre) {
       // Every position at or above the row's threshold bin was pre-read.
 #pragma unroll
@@ -1866,7 +1984,12 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
     }
   }
   if (fine) {
-    fine_tail<VEC>(a, g, slab, len, G, k, n_above, cnt, local_above, fine_lds, pf, sh, o, bad);
+    if (pre_done)
+      fine_tail<VEC>(a, g, slab, len, G, k, n_above, cnt, local_above, kFineMerged, pf, sh, o, bad || spec_bad,
+                     sstaged, sstaged_pg, (uint32_t)kSpecStageOff);
+    else
+      fine_tail<VEC>(a, g, slab, len, G, k, n_above, cnt, local_above, fine_lds ? kFineInLds : kFineGlobal, pf, sh,
+                     o, bad, sh.rhist, sh.outpos, (uint32_t)kStageCap);
     return;
   }
   merge_range(rg, sh);
@@ -1906,10 +2029,16 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
   // Last workgroup of the row: resolve the threshold bin, then leave the
   // row's state zeroed for the next call.
   if (found) resolve_split<VEC>(a, g, slab, keep, len, rowp, cut, k - n_above, cnt, n_above, sh, o);
+  if (EARLY && n_prop) {   // (early counts of a predicted bin)
+    uint64_t* fg = reinterpret_cast<uint64_t*>(g->fine);
+    for (int i = t; i < kFineBins / 2; i += kBlock) st_agent(fg + i, (uint64_t)0);
+    if (t < kFineGroups) st_agent(&g->fine_c[t], 0u);
+  }
   for (int r = t; r < kBins; r += kBlock) st_agent(&g->hist[r], 0u);
   if (t < 4) st_agent(&g->range[t], 0u);
   if (t == 0) {
-    st_agent(&g->arrive, 0u);
+    st_agent(&g->arrive, (uint64_t)0);
+    st_agent(&g->vsq, (uint64_t)0);
     st_agent(&g->emit, 0u);
     st_agent(&g->cand, 0u);
     st_agent(&g->done, 0u);
@@ -1927,7 +2056,7 @@ static_assert(kBins * kHistCopies * 4 <= kListCap / 2 * 8, "histogram copies fit
 // parked: this item's register tile is already in LDS (parked_tile).
 // STREAM: items longer than one register tile can occur (otherwise their code
 // is left out, which keeps it from weighing on the resident path's registers).
-template <bool VEC, bool STREAM>
+template <bool VEC, bool STREAM, bool EARLY>
 __device__ __forceinline__ void process_item(const SelectArgs& a, const WorkItem& item, Smem& sh, bool parked = false) {
   const int t = threadIdx.x;
   // (every field is uniform: held in scalar registers)
@@ -2013,7 +2142,7 @@ __device__ __forceinline__ void process_item(const SelectArgs& a, const WorkItem
   hist_copies_sum(hc, sh.lhist);
   __syncthreads();
   if (w.group < 0) owned_row<VEC, STREAM>(a, len, rowp, o, resident, hk, sh);
-  else split_row<VEC>(a, w, len, rowp, o, resident, hk, sh);
+  else split_row<VEC, EARLY>(a, w, len, rowp, o, resident, hk, sh);
 }
 
 // In-kernel planning for small batches: thread t holds row t. Every
@@ -2247,7 +2376,7 @@ __global__ void __launch_bounds__(kBlock) topk_select_kernel(SelectArgs a) {
     } else {
       slot = (it - (int)blockIdx.x) / (int)gridDim.x;
     }
-    process_item<VEC, STREAM>(a, sh.pl_items[slot], sh, parked && it == (int)blockIdx.x);
+    process_item<VEC, STREAM, (OVERLAP >= kEpt / 4)>(a, sh.pl_items[slot], sh, parked && it == (int)blockIdx.x);
     __syncthreads();
   }
 }

@@ -63,19 +63,31 @@ static_assert(sizeof(WorkItem) == 32, "work item is 32 bytes");
 // workgroup starts its exact selection from a finished digit histogram.
 constexpr int kFineBits = 13;
 constexpr int kFineBins = 1 << kFineBits;
+// The digits also add up in groups of 64 (coarse counts), which a reader
+// polls instead of the whole digit histogram.
+constexpr int kFineGroups = kFineBins / 64;
 
 // Cross-workgroup state of one split row. Left zeroed after every use.
 struct GroupState {
   uint32_t hist[kBins];   // merged 1,024-bin histogram
-  uint32_t arrive;        // scores of the row that no merged bin counts
+  // Added once per workgroup, each in one 64-bit atomic, so that the low
+  // halves join the merged histogram's completeness check. High halves: the
+  // workgroups that proposed a threshold bin (9 bits) and the sum of the
+  // proposals (bin + 1) above them; the sum of the squared proposals.
+  uint64_t arrive;        // low: scores of the row that no merged bin counts
   uint32_t emit;          // output cursor for scores above the threshold bin
   uint32_t cand;          // cursor into this row's candidate buffer
   uint32_t done;          // workgroups that finished emission
   uint32_t range[4];      // threshold-bin candidates: max key32, ~min key32, max pos, ~min pos
-  uint32_t pad[8];
+  uint32_t pad0[23];
+  uint64_t vsq;           // low: workgroups; on a cache line of its own (atomics to one line queue)
+  uint32_t pad1[30];
   uint32_t fine[kFineBins];   // threshold-bin candidates by FP32-key digit (large bins only)
+  uint32_t fine_c[kFineGroups];   // the same by digit group, added once the group's digits have landed
 };
-static_assert(sizeof(GroupState) == 4096 + 64 + 4 * kFineBins, "group state layout");
+static_assert(sizeof(GroupState) == 4096 + 256 + 4 * kFineBins + 4 * kFineGroups, "group state layout");
+// Workgroups per split row stay below 2^9 (the proposer count's field).
+constexpr int kMaxRowGroups = 511;
 
 // The device status word sits at workspace offset 0.
 constexpr size_t kStatusBytes = 256;

@@ -562,6 +562,18 @@ def _large_bin_rows(kind: str, seed: int):
             tie, rest = pos[500:5500], pos[5500:12500]
             row[tie] = np.float32(7.375)
             row[rest] = synth._f32(7.375 - (1 + st.below(7000, 100_000)) * 2.0 ** -21)
+        elif kind == "split_vote":
+            # The first quarter holds ten private bins of 200 scores each
+            # (20 + 4 b), 2,000 in all; the rest holds 5,000 cluster scores at
+            # 3.0, where the row's threshold lies. Chunks of the first quarter
+            # may predict a private bin and the others the cluster bin: either
+            # vote may decide the row, and a wrong one must fall back.
+            row[top] = synth._f32(st.normal(1000) - 20.0)   # (no scores above the private bins)
+            for b in range(10):
+                blk = 1000 * b + st.permutation(1000)[:200]
+                row[blk] = synth._f32(20.0 + 4.0 * b + st.uniform(200) * 0.01)
+            zpos = 10_000 + st.permutation(n - 10_000)[:5000]
+            row[zpos] = synth._f32(3.0 + st.below(5000, 600) * 2.0 ** -22)
         elif kind == "one_key":
             row[mid] = np.float32(7.25)
         elif kind == "neg_inf_bin":
@@ -589,7 +601,7 @@ def _large_bin_rows(kind: str, seed: int):
 
 
 @pytest.mark.parametrize("kind", ["cluster", "one_key", "big_tie", "big_tie_front", "neg_inf_bin", "zero_bin",
-                                  "pos_inf_bin"])
+                                  "pos_inf_bin", "split_vote"])
 @pytest.mark.parametrize("path,kw", [("multi", {"wg_per_row": 2}), ("multi", {"wg_per_row": 8}),
                                      ("multi", {"wg_per_row": 36})], ids=["wg2", "wg8", "wg36"])
 def test_split_row_large_threshold_bin(kind, path, kw):
