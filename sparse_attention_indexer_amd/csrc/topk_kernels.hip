@@ -258,11 +258,13 @@ constexpr int kStageCap = kListCap - kPreCap / 2;  // staged candidates below th
 // above at most kFineListOff staged candidates and below the position list.
 constexpr int kFineListOff = 8192;
 static_assert(kFineListOff + kFineBins / 2 <= kStageCap, "fine-digit counters below the position list");
+// The per-workgroup digit-group sums (128 words) follow the digit counters.
+constexpr int kFineGroupOff = kFineListOff + kFineBins / 2;   // (list entries)
 // A workgroup that classifies its chunk before the row's histogram is merged
 // (a predicted crowded threshold bin, see split_row) stages its outputs above
 // that bin (positions, then block-table entries) here, clear of the merged
 // histogram it is about to read into rhist and of the prefixes in outpos.
-constexpr int kSpecStageOff = kFineListOff + kFineBins / 2;
+constexpr int kSpecStageOff = kFineGroupOff + kFineGroups / 2;
 static_assert(kSpecStageOff + kMaxK <= kStageCap, "predicted-bin outputs below the position list");
 static_assert(kWideWords * 4 <= kListCap * 8, "first-digit histogram aliases the LDS list");
 static_assert(kMaxK <= kRadixBins, "above-threshold staging aliases rhist");
@@ -1428,22 +1430,21 @@ static_assert(kFineMaxCand % kLdsCopyWords == 0, "the rounded-up copy stays belo
 // 512 j + 64 w + lane: one instruction adds a whole group of 64 consecutive
 // digits, which the memory system merges per cache line (one digit per
 // instruction, hot digits shared by every workgroup of the row serialise
-// there instead), and the group's sum is a wave sum.
+// there instead); the group sums were counted in LDS with the digits
+// (lfine[kFineBins + group]), and lane j of wave w adds group 8 j + w.
 static_assert(kFineBins == 16 * kBlock && kFineGroups * 64 == kFineBins, "16 digit groups per wave");
 __device__ __forceinline__ void merge_fine(const uint32_t* lfine, GroupState* g) {
   const int t = threadIdx.x;
   const uint32_t w = uni((uint32_t)t >> 6);
-  uint32_t sum = 0;   // lane j holds the sum of the wave's group j
-#pragma unroll 1
+#pragma unroll 8
   for (int j = 0; j < kFineBins / kBlock; ++j) {
     const int d = j * kBlock + t;
     const uint32_t c = lfine[d];
     if (c) __hip_atomic_fetch_add(&g->fine[d], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t s = wave_sum_u32(c);
-    sum = lane() == (uint32_t)j ? s : sum;
   }
+  const uint32_t sum = lane() < 16u ? lfine[kFineBins + lane() * kWaves + w] : 0u;
   drain_memory();
-  if (sum)   // (lanes below 16 only)
+  if (sum)
     __hip_atomic_fetch_add(&g->fine_c[lane() * kWaves + w], sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -1783,7 +1784,8 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
       }
     }
     if (propose)
-      for (int i = t; i < kFineBins / 4; i += kBlock) reinterpret_cast<uint4*>(lfine)[i] = make_uint4(0u, 0u, 0u, 0u);
+      for (int i = t; i < (kFineBins + kFineGroups) / 4; i += kBlock)
+        reinterpret_cast<uint4*>(lfine)[i] = make_uint4(0u, 0u, 0u, 0u);
     if (n_pre <= (uint32_t)kPreCap) {
       uint64_t m = pm;
       while (m) {
@@ -1828,7 +1830,9 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
             },
             [&](uint32_t kk, int32_t e) {
               const uint64_t v = sf.key(kk, e);
-              atomicAdd(&lfine[min((uint32_t)(v >> sshift), (uint32_t)kFineBins - 1u)], 1u);
+              const uint32_t d = min((uint32_t)(v >> sshift), (uint32_t)kFineBins - 1u);
+              atomicAdd(&lfine[d], 1u);
+              atomicAdd(&lfine[kFineBins + (d >> 6)], 1u);
               const uint32_t c = atomicAdd(&sh.cur_list, 1u);
               const bool ok = c < (uint32_t)kFineListOff;
               if (ok) sh.list[c] = v;
@@ -1921,7 +1925,8 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
   __syncthreads();
   if (fine && !pre_done) {   // digit counters (every wave has read its local bins above)
     if (fine_lds)
-      for (int i = t; i < kFineBins / 4; i += kBlock) reinterpret_cast<uint4*>(lfine)[i] = make_uint4(0u, 0u, 0u, 0u);
+      for (int i = t; i < (kFineBins + kFineGroups) / 4; i += kBlock)
+        reinterpret_cast<uint4*>(lfine)[i] = make_uint4(0u, 0u, 0u, 0u);
     else if (t < kFineGroups)
       sh.lhist[t] = 0u;
     __syncthreads();
@@ -1954,6 +1959,7 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
         // (the first increment of a digit appends it: a uniform-address
         // append the compiler aggregates per wave)
         atomicAdd(&lfine[d], 1u);
+        atomicAdd(&lfine[kFineBins + (d >> 6)], 1u);
       } else {
         __hip_atomic_fetch_add(&g->fine[d], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         atomicAdd(&sh.lhist[d >> 6], 1u);
