@@ -14,7 +14,10 @@
 // query row, which the workgroup keeps in LDS. The epilogue folds each 32x32
 // block: a lane holds one key and 16 of the 32 heads of the block, so
 // ReLU, the head-gate weights and the head sum stay in the lane, and one
-// cross-half exchange adds the other 16 heads.
+// cross-half exchange adds the other 16 heads. The query rows sit in LDS
+// with their eight 16-byte chunks XOR-swizzled by the row's low three bits:
+// the 32 lanes of a half-wave read one chunk of 32 consecutive rows, 128
+// bytes apart, which would otherwise all fall in the same banks.
 #include <hip/hip_runtime.h>
 
 #include "indexer_logits.h"
@@ -93,9 +96,10 @@ __global__ void __launch_bounds__(kLgBlock, 2) mqa_logits_kernel(LogitsArgs a) {
   constexpr int H = 32 * HB;
   const int t = threadIdx.x;
   const int rows = a.tokens * H;
-  // Stage the query codes, the gate weights and the lengths.
+  // Stage the query codes (chunk c of row r at chunk c ^ (r & 7)), the gate
+  // weights and the lengths.
   for (int i = t; i < rows * kDim / 16; i += kLgBlock)
-    reinterpret_cast<uint4*>(qs)[i] = reinterpret_cast<const uint4*>(a.q)[i];
+    reinterpret_cast<uint4*>(qs)[(i & ~7) | ((i & 7) ^ ((i >> 3) & 7))] = reinterpret_cast<const uint4*>(a.q)[i];
   for (int i = t; i < rows; i += kLgBlock) ws[i] = a.w[i];
   if (t < a.tokens) lens[t] = min(a.lengths[t], a.max_len);
   __syncthreads();
@@ -103,6 +107,11 @@ __global__ void __launch_bounds__(kLgBlock, 2) mqa_logits_kernel(LogitsArgs a) {
   const int l = t & 63;
   const int n = l & 31;          // this lane's key within the step (B column, C column)
   const int half = l >> 5;       // which 32 of each 64-deep block (A/B), which 4-row group (C)
+  // Byte offsets of the lane's four A chunks (2 half, +1, +4, +5) in its
+  // swizzled query row: every row it reads has row & 7 == n & 7.
+  const int sw = n & 7;
+  const int c0 = ((2 * half) ^ sw) * 16, c1 = ((2 * half + 1) ^ sw) * 16;
+  const int c2 = ((2 * half + 4) ^ sw) * 16, c3 = ((2 * half + 5) ^ sw) * 16;
   const int64_t steps = ((int64_t)a.max_len + kKeysPerStep - 1) / kKeysPerStep;
   const int64_t stride = (int64_t)gridDim.x * kLgWaves;
   int64_t step = (int64_t)blockIdx.x * kLgWaves + (t >> 6);
@@ -117,9 +126,9 @@ __global__ void __launch_bounds__(kLgBlock, 2) mqa_logits_kernel(LogitsArgs a) {
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
         // A: query rows tok*H + 32 hb + (0..31), the same dims as the key operand
-        const uint8_t* qr = qs + (size_t)(tok * H + 32 * hb + n) * kDim + half * 32;
-        const uint4 y0 = *reinterpret_cast<const uint4*>(qr), y1 = *reinterpret_cast<const uint4*>(qr + 16);
-        const uint4 y2 = *reinterpret_cast<const uint4*>(qr + 64), y3 = *reinterpret_cast<const uint4*>(qr + 80);
+        const uint8_t* qr = qs + (size_t)(tok * H + 32 * hb + n) * kDim;
+        const uint4 y0 = *reinterpret_cast<const uint4*>(qr + c0), y1 = *reinterpret_cast<const uint4*>(qr + c1);
+        const uint4 y2 = *reinterpret_cast<const uint4*>(qr + c2), y3 = *reinterpret_cast<const uint4*>(qr + c3);
         const v8i a0 = {(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w, (int)y1.x, (int)y1.y, (int)y1.z, (int)y1.w};
         const v8i a1 = {(int)y2.x, (int)y2.y, (int)y2.z, (int)y2.w, (int)y3.x, (int)y3.y, (int)y3.z, (int)y3.w};
         acc[hb] = v16f{};
