@@ -2062,7 +2062,8 @@ static_assert(kBins * kHistCopies * 4 <= kListCap / 2 * 8, "histogram copies fit
 // parked: this item's register tile is already in LDS (parked_tile).
 // STREAM: items longer than one register tile can occur (otherwise their code
 // is left out, which keeps it from weighing on the resident path's registers).
-template <bool VEC, bool STREAM, bool EARLY>
+// PQ: vector groups a parked tile holds (the rest of it is NaN padding).
+template <bool VEC, bool STREAM, bool EARLY, int PQ>
 __device__ __forceinline__ void process_item(const SelectArgs& a, const WorkItem& item, Smem& sh, bool parked = false) {
   const int t = threadIdx.x;
   // (every field is uniform: held in scalar registers)
@@ -2123,7 +2124,7 @@ __device__ __forceinline__ void process_item(const SelectArgs& a, const WorkItem
     if (parked) {
       const uint32_t* pt = parked_tile(sh);
 #pragma unroll
-      for (int i = 0; i < kHk; ++i) hk[i] = pt[i * kBlock + t];
+      for (int i = 0; i < kHk; ++i) hk[i] = i < 2 * PQ ? pt[i * kBlock + t] : kHalfNaN2;
     } else {
       float4 x[kEpt / 4];
       load_raw<VEC>(rowp, begin, end, x);
@@ -2336,9 +2337,11 @@ __device__ __forceinline__ bool guess_and_plan(const SelectArgs& a, Smem& sh, in
       uint32_t hk[kHk];
       // (OVERLAP > 0: a guessed chunk spans at most OVERLAP vector groups)
       pack_hist<(OVERLAP > 0 ? OVERLAP : kEpt / 4)>(x, sbeg, end0, hk, reinterpret_cast<uint32_t*>(sh.list));
+      // (only the vector groups the guess spans: the rest are NaN padding,
+      // which the unparking rebuilds)
       uint32_t* pt = parked_tile(sh);
 #pragma unroll
-      for (int i = 0; i < kHk; ++i) pt[i * kBlock + threadIdx.x] = hk[i];
+      for (int i = 0; i < 2 * (OVERLAP > 0 ? OVERLAP : kEpt / 4); ++i) pt[i * kBlock + threadIdx.x] = hk[i];
     }
   }
   return parked;
@@ -2382,7 +2385,8 @@ __global__ void __launch_bounds__(kBlock) topk_select_kernel(SelectArgs a) {
     } else {
       slot = (it - (int)blockIdx.x) / (int)gridDim.x;
     }
-    process_item<VEC, STREAM, (OVERLAP >= kEpt / 4)>(a, sh.pl_items[slot], sh, parked && it == (int)blockIdx.x);
+    process_item<VEC, STREAM, (OVERLAP >= kEpt / 4), (OVERLAP > 0 ? OVERLAP : kEpt / 4)>(
+        a, sh.pl_items[slot], sh, parked && it == (int)blockIdx.x);
     __syncthreads();
   }
 }
