@@ -1604,26 +1604,29 @@ __device__ __forceinline__ void fine_tail(const SelectArgs& a, GroupState* g, ui
   __syncthreads();
   // Stores: the outputs (table entries of the selected candidates read now,
   // in flight with the reservation's round trip) and the survivors.
+  // (survivors first: only they must have landed before the arrival count;
+  // waves 1 to 7 store the outputs during the round trip of `done`)
   const uint32_t n_out = room ? n_above_loc + tsel : n_above_loc;
   const uint32_t bo = uni(sh.bcast[0]), bc = uni(sh.bcast[1]);
-  for (uint32_t i = t; i < n_out; i += kBlock) {
-    const int32_t e = (int32_t)staged[i];
-    const int32_t pg = i < n_above_loc ? (int32_t)staged_pg[i] : ((uint32_t)e < (uint32_t)len ? o.page(e) : 0);
-    bad |= !o.store_page(bo + i, e, pg);
-  }
   if (room && stage_surv)
     for (uint32_t i = t; i < tkeep; i += kBlock) {
       const bool fits = (int64_t)(bc + i) < a.cand_cap;
       if (fits) st_agent(slab + bc + i, sh.list[surv_off + i]);
       bad |= !fits;
     }
-  report_bad(bad, a.status);
   drain_memory();
   __syncthreads();
   if (t == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(&g->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sh.flag = prev == G - 1u;
+  } else if (t >= kWave) {
+    for (uint32_t i = t - kWave; i < n_out; i += kBlock - kWave) {
+      const int32_t e = (int32_t)staged[i];
+      const int32_t pg = i < n_above_loc ? (int32_t)staged_pg[i] : ((uint32_t)e < (uint32_t)len ? o.page(e) : 0);
+      bad |= !o.store_page(bo + i, e, pg);
+    }
   }
+  report_bad(bad, a.status);
   __syncthreads();
   if (!uni(sh.flag)) return;
   // The last workgroup: d*'s survivors (cnt_d, all in the list now) resolved
@@ -2011,10 +2014,12 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
     }
   }
   __syncthreads();
-  // Staged outputs and candidates leave in consecutive, coalesced stores.
+  // Staged candidates, then outputs, leave in consecutive, coalesced stores.
+  // Only the candidates must have landed before the arrival count (the last
+  // workgroup reads them); no workgroup reads the outputs, so waves 1 to 7
+  // store them while wave 0 makes the round trip of `done`.
   const uint32_t bo = uni(sh.bcast[0]), bc = uni(sh.bcast[1]);
   const uint32_t n_out = min(uni(sh.cur_out), (uint32_t)kMaxK);
-  for (uint32_t i = t; i < n_out; i += kBlock) bad |= !o.store_page(bo + i, (int32_t)staged[i], (int32_t)staged_pg[i]);
   if (stage) {
     const uint32_t n_c = min(uni(sh.cur_list), (uint32_t)kStageCap);
     for (uint32_t i = t; i < n_c; i += kBlock) {
@@ -2023,13 +2028,16 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
       bad |= !ok;
     }
   }
-  report_bad(bad, a.status);
   drain_memory();
   __syncthreads();
   if (t == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(&g->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sh.flag = prev == G - 1;
+  } else if (t >= kWave) {
+    for (uint32_t i = t - kWave; i < n_out; i += kBlock - kWave)
+      bad |= !o.store_page(bo + i, (int32_t)staged[i], (int32_t)staged_pg[i]);
   }
+  report_bad(bad, a.status);
   __syncthreads();
   if (!uni(sh.flag)) return;
   // Last workgroup of the row: resolve the threshold bin, then leave the
