@@ -1848,20 +1848,32 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
   // Read the merged bins and the rest count until they add up to the row
   // length. Every contribution is a non-negative add, so each value read is
   // at most its final value; a read that sums to the final total therefore
-  // read every final value: a consistent snapshot of the merge.
+  // read every final value: a consistent snapshot of the merge. Lane t reads
+  // the ordered bins 1023 - 2 t and 1022 - 2 t, so the poll's own prefix sum
+  // is the count above the lane's bins and the threshold search needs no
+  // second scan; the rest count and the vote word go to the last lane, whose
+  // bins are the lowest (no bin's prefix includes them).
+  static_assert(kBins == 2 * kBlock, "two bins per lane");
+  static_assert(offsetof(GroupState, vsq) == offsetof(GroupState, arrive) + 128, "vote word one line past arrive");
+  const uint32_t ob0 = (uint32_t)(kBins - 1 - 2 * t), ob1 = ob0 - 1u;
+  const uint32_t pr0 = raw_of_bin(ob0), pr1 = raw_of_bin(ob1);
+  uint32_t ph0 = 0, ph1 = 0, pcum = 0;
+  if (t == 0) sh.res[0] = kNotFound;   // (ordered before the search by the poll's barriers)
   {
-    static_assert(kBins == 2 * kBlock, "two bins per lane");
     // At most spin_limit polls (uniform); a limit of 0 gives up at once.
     bool ok = false;
-    static_assert(offsetof(GroupState, vsq) == offsetof(GroupState, arrive) + 128, "vote word one line past arrive");
     for (uint32_t spins = 0; spins < a.spin_limit; ++spins) {
-      const uint32_t h0 = ld_agent(&g->hist[t]), h1 = ld_agent(&g->hist[t + kBlock]);
-      const uint64_t v = t < (EARLY ? 2 : 1) ? ld_agent(&g->arrive + 16 * t) : (uint64_t)0;
-      sh.rhist[t] = h0;
-      sh.rhist[t + kBlock] = h1;
-      if (t < 2) sh.pl_red2[t] = (uint32_t)(v >> 32);
+      ph0 = ld_agent(&g->hist[pr0]);
+      ph1 = ld_agent(&g->hist[pr1]);
+      const bool last = t == kBlock - 1;
+      const uint64_t va = last ? ld_agent(&g->arrive) : (uint64_t)0;
+      const uint64_t vq = EARLY && last ? ld_agent(&g->vsq) : (uint64_t)0;
+      if (last) {
+        sh.pl_red2[0] = (uint32_t)(va >> 32);
+        sh.pl_red2[1] = (uint32_t)(vq >> 32);
+      }
       uint32_t tot;
-      block_exclusive_add(h0 + h1 + (uint32_t)v, sh.scratch, &tot);
+      pcum = block_exclusive_add(ph0 + ph1 + (uint32_t)va + (uint32_t)vq, sh.scratch, &tot);
       if (uni(tot) == (uint32_t)len + (EARLY ? G : 0u)) {   // (the rest count, then one per workgroup)
         ok = true;
         break;
@@ -1874,11 +1886,17 @@ __device__ __forceinline__ void split_row(const SelectArgs& a, const WorkItem& w
     }
   }
   // Bins at or above the largest chunk threshold are complete, and the row's
-  // threshold bin lies there, so the scan from the top is exact. Not found
-  // only with NaN inputs; the workgroup then skips its emission but still
-  // takes part in the arrival count so the row's state is reset.
-  if (t == 0) sh.res[0] = kNotFound;
-  find_threshold_raw(sh.rhist, k, sh.scratch, sh.res);
+  // threshold bin lies there, so the count from the top is exact (NaN bins
+  // are never merged and read 0). Not found only with NaN inputs; the
+  // workgroup then skips its emission but still takes part in the arrival
+  // count so the row's state is reset.
+  if (pcum < k && k <= pcum + ph0 + ph1) {
+    const bool hi = k <= pcum + ph0;
+    sh.res[0] = hi ? ob0 : ob1;
+    sh.res[1] = hi ? pcum : pcum + ph0;
+    sh.res[2] = hi ? ph0 : ph1;
+  }
+  __syncthreads();
   const uint32_t r0 = uni(sh.res[0]);
   const bool found = r0 != kNotFound;
   if (!found && t == 0) atomicOr(a.status, TOPK_DEVICE_INTERNAL);
