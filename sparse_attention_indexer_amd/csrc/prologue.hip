@@ -131,20 +131,23 @@ __device__ __forceinline__ void key_token(const KeyArgs& a, int sub, int32_t pos
 }
 
 // Each 16-lane group takes kTokensPerGroup consecutive tokens and issues the
-// loads of all of them before using any (three dependent steps: the token's
-// position and row; its activations, table entry and rotary row; the
-// arithmetic).
+// loads of all of them before using any: the activations (addressed by the
+// token index alone) go out with the token's position and row, and only
+// the table entry and rotary row wait for those; then the arithmetic.
 __global__ void __launch_bounds__(kPrologueBlock) key_prologue_kernel(KeyArgs a) {
   const int sub = (int)(threadIdx.x & (kLanesPerToken - 1));
   const int64_t tok0 = ((int64_t)blockIdx.x * kGroupsPerBlock + (threadIdx.x / kLanesPerToken)) * kTokensPerGroup;
   int32_t row[kTokensPerGroup], pos[kTokensPerGroup];
   bool live[kTokensPerGroup];
+  uint4 raw[kTokensPerGroup];
 #pragma unroll
   for (int u = 0; u < kTokensPerGroup; ++u) {
     const int64_t tok = tok0 + u;
     const bool in = tok < a.num_tokens;
     row[u] = in ? (a.token_row ? a.token_row[tok] : 0) : -1;
     pos[u] = in ? a.positions[tok] : 0;
+    raw[u] = in ? *reinterpret_cast<const uint4*>(a.k_act + tok * a.k_stride + sub * kDimsPerLane)
+                : make_uint4(0u, 0u, 0u, 0u);
   }
   // (every test below is uniform over the token's 16 lanes)
 #pragma unroll
@@ -160,17 +163,14 @@ __global__ void __launch_bounds__(kPrologueBlock) key_prologue_kernel(KeyArgs a)
   const float4 b0 = *reinterpret_cast<const float4*>(a.bias + sub * kDimsPerLane);
   const float4 b1 = *reinterpret_cast<const float4*>(a.bias + sub * kDimsPerLane + 4);
   const bool rot = sub * kDimsPerLane < a.rope_dim;   // this lane's 4 pairs are rotated
-  uint4 raw[kTokensPerGroup];
   int32_t page[kTokensPerGroup];
   float4 c[kTokensPerGroup], s[kTokensPerGroup];
 #pragma unroll
   for (int u = 0; u < kTokensPerGroup; ++u) {
-    raw[u] = make_uint4(0u, 0u, 0u, 0u);
     page[u] = 0;
     c[u] = make_float4(1.f, 1.f, 1.f, 1.f);
     s[u] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (live[u]) {
-      raw[u] = *reinterpret_cast<const uint4*>(a.k_act + (tok0 + u) * a.k_stride + sub * kDimsPerLane);
       page[u] = a.table[(int64_t)row[u] * a.table_stride + pos[u] / a.page_size];
       if (rot) {
         const float* cs = a.cos_sin + (int64_t)pos[u] * a.rope_dim + sub * (kDimsPerLane / 2);
@@ -208,13 +208,16 @@ __global__ void __launch_bounds__(kPrologueBlock) query_prologue_kernel(QueryArg
   const int sub = (int)(threadIdx.x & (kLanesPerToken - 1));
   const int64_t r = (int64_t)blockIdx.x * kGroupsPerBlock + (threadIdx.x / kLanesPerToken);
   if (r >= a.rows) return;   // (uniform over the row's 16 lanes)
+  // (the codes and the gate weight go out with the position; only the
+  // rotary row waits for it)
   const int32_t pos = a.positions[r / a.heads];
+  const uint4 raw = *reinterpret_cast<const uint4*>(a.q + r * kKeyDim + sub * kDimsPerLane);
+  const float w_raw = sub == 0 ? a.w_raw[r] : 0.f;
   const bool rot = sub * kDimsPerLane < a.rope_dim;
   if (a.rope_dim > 0 && (pos < 0 || pos >= a.max_pos)) {
     if (sub == 0 && a.status) atomicOr(a.status, INDEXER_DEVICE_BAD_POSITION);
     return;
   }
-  const uint4 raw = *reinterpret_cast<const uint4*>(a.q + r * kKeyDim + sub * kDimsPerLane);
   float4 c = make_float4(1.f, 1.f, 1.f, 1.f), s = make_float4(0.f, 0.f, 0.f, 0.f);
   if (rot) {
     const float* cs = a.cos_sin + (int64_t)pos * a.rope_dim + sub * (kDimsPerLane / 2);
@@ -248,7 +251,7 @@ __global__ void __launch_bounds__(kPrologueBlock) query_prologue_kernel(QueryArg
   *reinterpret_cast<uint2*>(a.q_codes + r * kKeyDim + sub * kDimsPerLane) = make_uint2((uint32_t)lo, (uint32_t)hi);
   if (sub == 0) {
     const float q_scale = amax / kE4M3Max;
-    a.w_out[r] = (a.w_raw[r] * q_scale) * a.gate_scale;
+    a.w_out[r] = (w_raw * q_scale) * a.gate_scale;
   }
 }
 
