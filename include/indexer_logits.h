@@ -28,7 +28,8 @@
  * share every key: tokens * heads <= INDEXER_LOGITS_MAX_QROWS query rows,
  * heads 32, 64 or 128, D = 128, one request per call (block_table is that
  * request's row). Entries out[t][s] for s >= min(lengths[t], max_len) are
- * not written.
+ * not written. Codes are finite E4M3 values: a score whose query or key
+ * holds the NaN code (0x7F or 0xFF) is unspecified.
  *
  * Memory, threading, errors
  * -------------------------

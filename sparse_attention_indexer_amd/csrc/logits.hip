@@ -44,6 +44,7 @@ struct LogitsArgs {
   const float* k_scale;    // [slots]
   const int32_t* table;    // the request's block-table row
   int32_t page_size;
+  int32_t page_shift;      // log2(page_size) when a power of two, else -1
   int64_t num_slots;
   const int32_t* lengths;  // [T]
   int32_t max_len;         // max over lengths (host-supplied bound)
@@ -68,8 +69,9 @@ __device__ __forceinline__ KeyStep load_keys(const LogitsArgs& a, int32_t s, int
   k.ok = false;
   k.bad = false;
   if (s < a.max_len) {
-    const int32_t page = a.table[s / a.page_size];
-    const int64_t slot = (int64_t)page * a.page_size + s % a.page_size;
+    const int32_t page = a.table[a.page_shift >= 0 ? s >> a.page_shift : s / a.page_size];
+    const int64_t slot =
+        (int64_t)page * a.page_size + (a.page_shift >= 0 ? s & (a.page_size - 1) : s % a.page_size);
     if (page < 0 || slot >= a.num_slots) {
       k.bad = true;
     } else {
@@ -150,7 +152,10 @@ __global__ void __launch_bounds__(kLgBlock, 2) mqa_logits_kernel(LogitsArgs a) {
           total += wv.w * fmaxf(acc[hb][4 * g + 3], 0.f);
         }
       }
-      total += __shfl_xor(total, 32);   // the other 16 heads of each block, same key
+      // The other 16 heads of each block, same key: after the swap, lane n < 32
+      // holds its own total and lane n + 32's.
+      const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(total), __float_as_uint(total), false, false);
+      total = __uint_as_float(sw2[0]) + __uint_as_float(sw2[1]);
       if (half == 0 && cur.ok && s < lens[tok]) a.out[(int64_t)tok * a.out_stride + s] = total * cur.scale;
     }
     cur = nxt;
@@ -185,6 +190,7 @@ topk_status indexer_mqa_logits(const uint8_t* q_codes, const float* w, int32_t t
   a.k_scale = k_scale;
   a.table = block_table;
   a.page_size = page_size;
+  a.page_shift = (page_size & (page_size - 1)) == 0 ? __builtin_ctz((unsigned)page_size) : -1;
   a.num_slots = num_slots;
   a.lengths = lengths;
   a.max_len = max_len;

@@ -75,6 +75,10 @@ CASES = [
     dict(tokens=8, keys=5000, heads=64, page_size=1),
     dict(tokens=16, keys=700, heads=32),      # tokens x heads = 512, the maximum
     dict(tokens=2, keys=40_000, heads=128),
+    dict(tokens=1, keys=3000, heads=64),
+    dict(tokens=2, keys=2100, heads=64, page_size=16),
+    dict(tokens=3, keys=1500, heads=64, page_size=48),   # a page size that is not a power of two
+    dict(tokens=5, keys=2000, heads=32),
 ]
 
 
@@ -91,6 +95,14 @@ def test_mqa_logits_full_size_sampled():
     w = synth.make_logits(7, 1_000_000, seed=22, with_table=False)
     _gpu.say("[logits] 7 x 1,000,000 sampled")
     check_logits(w, "7x1M", sample=20_000)
+
+
+def test_mqa_logits_many_tiles_sampled():
+    """Many key steps per wave of the persistent grid, 32 heads, a page size
+    other than the default."""
+    w = synth.make_logits(6, 150_000, heads=32, page_size=32, seed=23, with_table=False)
+    _gpu.say("[logits] 6 x 150,000 x 32 heads sampled")
+    check_logits(w, "6x150K", sample=5000)
 
 
 def test_mqa_logits_limits_and_flags():
