@@ -1320,7 +1320,35 @@ __device__ __forceinline__ void owned_row(const SelectArgs& a, int32_t len, cons
     // and only its few such positions are re-read.
     const bool dense = (uint64_t)(n_above + cnt) * 8u > (uint64_t)len;
     for (int32_t base = 0; base < len; base += kTile) {
-      if (dense) {
+      if (VEC && dense && !use_list) {
+        // Every score is classified without branches: the above-threshold
+        // ones are written through one wave-aggregated cursor add, the
+        // candidates counted by digit (one add per wave when the lanes share
+        // the digit), and only the key range is kept (the exact passes use
+        // the fine frame, not the candidates' position range). (Rows read
+        // with scalar loads keep the branching form, which needs no scratch
+        // there.)
+        float4 x[kEpt / 4];
+        load_raw<VEC>(rowp, base, len, x);
+#pragma unroll
+        for (int q = 0; q < kEpt / 4; ++q) {
+          const float xs[4] = {x[q].x, x[q].y, x[q].z, x[q].w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int32_t e = tile_pos(base, q, c);
+            const _Float16 h = half_lo(to_half2(xs[c], xs[c]));
+            const bool in = e < len;
+            const bool above = in && h >= cut.vhi;
+            const bool cand = in && !(h >= cut.vhi) && h >= cut.vlo;
+            bad |= !emit_wave(above, e, &sh.cur_out, o);
+            const uint32_t kk = key32_of(xs[c]);
+            rg.kmax = max(rg.kmax, cand ? kk : 0u);
+            rg.kmin_inv = max(rg.kmin_inv, cand ? ~kk : 0u);
+            const uint32_t d = (kk - pf.lo32) >> fshift;
+            hist_add(whist, cand, d + (d >> kWidePad));
+          }
+        }
+      } else if (dense) {
         float4 x[kEpt / 4];
         load_raw<VEC>(rowp, base, len, x);
 #pragma unroll
