@@ -859,6 +859,7 @@ constexpr uint32_t kFineMin = 4096;
 
 // Composite keys already in LDS.
 struct KeyListSrc {
+  static constexpr bool kStream = false;
   const uint64_t* p;
   uint32_t n;
   template <class F>
@@ -874,6 +875,7 @@ struct KeyListSrc {
 // (key32 << 32 | position) pairs that other workgroups left in global memory,
 // read with device-coherent loads.
 struct PairListSrc {
+  static constexpr bool kStream = false;
   const uint64_t* p;
   uint32_t n;
   Refine r;
@@ -894,12 +896,81 @@ struct PairListSrc {
 // short round trips.
 constexpr int kStreamVec = 8;
 
-template <bool VEC>
+// FIRST: the first emission pass takes emit_first_digit (the streamed kernel
+// variants' owned rows; elsewhere it would only add registers).
+template <bool VEC, bool FIRST = false>
 struct StreamSrc {
+  static constexpr bool kStream = FIRST;
   const float* rowp;
   int32_t begin, end;
   Cut cut;
   Refine r;
+  // The exact selection's first emission pass over the row when its digit
+  // lies above the position bits (key offset >> ks, masked; the frame holds
+  // offsets below 2^kw): scores in the frame with a digit above d (or equal
+  // to it when `finish`) are output, those equal to d kept in `list` when
+  // `compact`. Each step's outputs and kept keys are reserved with one
+  // cursor add per wave (a wave prefix of the lanes' counts) instead of one
+  // per element, whose round trip each element would otherwise wait for.
+  template <class O>
+  __device__ __forceinline__ bool emit_first_digit(uint32_t ks, uint32_t kw, uint32_t mask, uint32_t d, bool finish,
+                                                   bool compact, uint32_t* cur_out, uint32_t* cur_list,
+                                                   uint64_t* list, const O& o) const {
+    constexpr int V = kStreamVec / 2;   // (16 scores per reservation: fewer live registers)
+    static_assert(V * 4 <= 32, "one bit per element of a step");
+    bool bad = false;
+    for (int32_t base = begin; base < end; base += V * kBlock * 4) {
+      float x[V * 4];
+#pragma unroll
+      for (int u = 0; u < V; ++u) {
+        const int32_t e = base + (u * kBlock + (int)threadIdx.x) * 4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) x[u * 4 + c] = 0.f;
+        if constexpr (VEC) {
+          if (e < end) {
+            const float4 v = *reinterpret_cast<const float4*>(rowp + e);
+            x[u * 4 + 0] = v.x;
+            x[u * 4 + 1] = v.y;
+            x[u * 4 + 2] = v.z;
+            x[u * 4 + 3] = v.w;
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (e + c < end) x[u * 4 + c] = rowp[e + c];
+        }
+      }
+      uint32_t tm = 0, km = 0;   // bit j: element j is output / kept
+#pragma unroll
+      for (int j = 0; j < V * 4; ++j) {
+        const int32_t e = base + ((j >> 2) * kBlock + (int)threadIdx.x) * 4 + (j & 3);
+        const _Float16 h = half_lo(to_half2(x[j], 0.f));
+        const bool in_bin = e < end && h >= cut.vlo && !(h >= cut.vhi);
+        const uint32_t off = key32_of(x[j]) - r.lo32;
+        const bool m = in_bin && (uint64_t)off < (1ull << kw);
+        const uint32_t dig = (off >> ks) & mask;
+        tm |= (uint32_t)(m && (dig > d || (finish && dig == d))) << j;
+        km |= (uint32_t)(compact && m && dig == d) << j;
+      }
+      const uint32_t nt = (uint32_t)__popc(tm), nk = (uint32_t)__popc(km);
+      const uint32_t it = wave_inclusive_add(nt), ik = wave_inclusive_add(nk);
+      const uint32_t tt = read_lane(it, kWave - 1), tk = read_lane(ik, kWave - 1);
+      if ((tt | tk) == 0) continue;   // (uniform)
+      uint32_t bt = 0, bk = 0;
+      if (lane() == 0) {
+        if (tt) bt = atomicAdd(cur_out, tt);
+        if (tk) bk = atomicAdd(cur_list, tk);
+      }
+      uint32_t ot = read_lane(bt, 0) + it - nt, ok = read_lane(bk, 0) + ik - nk;
+#pragma unroll
+      for (int j = 0; j < V * 4; ++j) {
+        const int32_t e = base + ((j >> 2) * kBlock + (int)threadIdx.x) * 4 + (j & 3);
+        if ((tm >> j) & 1u) bad |= !o.write(ot++, e);
+        if ((km >> j) & 1u) list[ok++] = r.key(key32_of(x[j]), e);
+      }
+    }
+    return bad;
+  }
   template <class F>
   __device__ __forceinline__ void each(F&& f) const {
     for (int32_t base = begin; base < end; base += kStreamVec * kBlock * 4) {
@@ -1030,8 +1101,21 @@ __device__ __forceinline__ void refine(const Src& src, const Refine& p, Smem& sh
       bad |= !emit_wave(m && (dig > d || (finish && dig == d)), p.pos(ck), &sh.cur_out, o);
       if (compact) push_wave(m && dig == d, ck, &sh.cur_list, sh.list);
     };
-    if (in_list) KeyListSrc{sh.list + list_off, list_n}.each(emit_fn);
-    else src.each(emit_fn);
+    bool emitted = false;
+    if constexpr (Src::kStream) {
+      // The first pass over a streamed row, its digit above the position
+      // bits (prefix empty, so only the frame test remains): per-step
+      // reservations (StreamSrc::emit_first_digit).
+      if (!in_list && pbits == 0 && shift >= p.b2) {
+        bad |= src.emit_first_digit(shift - p.b2, p.nb - p.b2, mask, d, finish, compact, &sh.cur_out, &sh.cur_list,
+                                    sh.list, o);
+        emitted = true;
+      }
+    }
+    if (!emitted) {
+      if (in_list) KeyListSrc{sh.list + list_off, list_n}.each(emit_fn);
+      else src.each(emit_fn);
+    }
     __syncthreads();
     if (finish) break;
     need -= above;
@@ -1380,7 +1464,7 @@ __device__ __forceinline__ void owned_row(const SelectArgs& a, int32_t len, cons
     Refine q = pf;
     q.need = need;
     q.cnt = cnt;
-    refine<false>(StreamSrc<VEC>{rowp, 0, len, cut, q}, q, sh, o, 0ull, 0u, need, cnt, true);
+    refine<false>(StreamSrc<VEC, STREAM>{rowp, 0, len, cut, q}, q, sh, o, 0ull, 0u, need, cnt, true);
   } else if (cnt <= (uint32_t)(kRegSmall * kBlock)) {
     resolve_lds_pairs<kRegSmall>(cnt, p, sh, o);
   } else if (cnt <= (uint32_t)(kRegMid * kBlock)) {
