@@ -916,11 +916,11 @@ struct StreamSrc {
   __device__ __forceinline__ bool emit_first_digit(uint32_t ks, uint32_t kw, uint32_t mask, uint32_t d, bool finish,
                                                    bool compact, uint32_t* cur_out, uint32_t* cur_list,
                                                    uint64_t* list, const O& o) const {
-    constexpr int V = kStreamVec / 2;   // (16 scores per reservation: fewer live registers)
+    constexpr int V = kStreamVec / 2;   // 16 scores per lane and reservation
+    constexpr int32_t kSpan = V * kBlock * 4;
     static_assert(V * 4 <= 32, "one bit per element of a step");
     bool bad = false;
-    for (int32_t base = begin; base < end; base += V * kBlock * 4) {
-      float x[V * 4];
+    auto load = [&](float (&x)[V * 4], int32_t base) {
 #pragma unroll
       for (int u = 0; u < V; ++u) {
         const int32_t e = base + (u * kBlock + (int)threadIdx.x) * 4;
@@ -940,6 +940,8 @@ struct StreamSrc {
             if (e + c < end) x[u * 4 + c] = rowp[e + c];
         }
       }
+    };
+    auto use = [&](const float (&x)[V * 4], int32_t base) {
       uint32_t tm = 0, km = 0;   // bit j: element j is output / kept
 #pragma unroll
       for (int j = 0; j < V * 4; ++j) {
@@ -955,7 +957,7 @@ struct StreamSrc {
       const uint32_t nt = (uint32_t)__popc(tm), nk = (uint32_t)__popc(km);
       const uint32_t it = wave_inclusive_add(nt), ik = wave_inclusive_add(nk);
       const uint32_t tt = read_lane(it, kWave - 1), tk = read_lane(ik, kWave - 1);
-      if ((tt | tk) == 0) continue;   // (uniform)
+      if ((tt | tk) == 0) return;   // (uniform)
       uint32_t bt = 0, bk = 0;
       if (lane() == 0) {
         if (tt) bt = atomicAdd(cur_out, tt);
@@ -968,6 +970,21 @@ struct StreamSrc {
         if ((tm >> j) & 1u) bad |= !o.write(ot++, e);
         if ((km >> j) & 1u) list[ok++] = r.key(key32_of(x[j]), e);
       }
+    };
+    // The next step's loads are in flight while a step is used (two register
+    // sets, the loop unrolled twice so that neither is copied).
+    float xa[V * 4], xb[V * 4];
+    int32_t base = begin;
+    load(xa, base);
+    for (;;) {
+      if (base >= end) break;
+      load(xb, base + kSpan);
+      use(xa, base);
+      base += kSpan;
+      if (base >= end) break;
+      load(xa, base + kSpan);
+      use(xb, base);
+      base += kSpan;
     }
     return bad;
   }
