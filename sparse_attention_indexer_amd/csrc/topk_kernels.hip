@@ -1434,19 +1434,36 @@ __device__ __forceinline__ void owned_row(const SelectArgs& a, int32_t len, cons
 #pragma unroll
         for (int q = 0; q < kEpt / 4; ++q) {
           const float xs[4] = {x[q].x, x[q].y, x[q].z, x[q].w};
+          bool above[4], cand[4];
+          uint32_t dp[4];   // padded digit slots
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const int32_t e = tile_pos(base, q, c);
             const _Float16 h = half_lo(to_half2(xs[c], xs[c]));
             const bool in = e < len;
-            const bool above = in && h >= cut.vhi;
-            const bool cand = in && !(h >= cut.vhi) && h >= cut.vlo;
-            bad |= !emit_wave(above, e, &sh.cur_out, o);
+            above[c] = in && h >= cut.vhi;
+            cand[c] = in && !(h >= cut.vhi) && h >= cut.vlo;
             const uint32_t kk = key32_of(xs[c]);
-            rg.kmax = max(rg.kmax, cand ? kk : 0u);
-            rg.kmin_inv = max(rg.kmin_inv, cand ? ~kk : 0u);
+            rg.kmax = max(rg.kmax, cand[c] ? kk : 0u);
+            rg.kmin_inv = max(rg.kmin_inv, cand[c] ? ~kk : 0u);
             const uint32_t d = (kk - pf.lo32) >> fshift;
-            hist_add(whist, cand, d + (d >> kWidePad));
+            dp[c] = d + (d >> kWidePad);
+          }
+          // (per vector: the outputs only where a lane has one, and one add
+          // per wave when every lane's four scores share a digit)
+          if (__ballot(above[0] || above[1] || above[2] || above[3])) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) bad |= !emit_wave(above[c], tile_pos(base, q, c), &sh.cur_out, o);
+          }
+          const uint32_t f = (uint32_t)__builtin_amdgcn_readfirstlane((int)dp[0]);
+          const bool same = cand[0] && cand[1] && cand[2] && cand[3] && dp[0] == f && dp[1] == f && dp[2] == f &&
+                            dp[3] == f;
+          if (__ballot(same) == ~0ull) {
+            if (lane() == 0) atomicAdd(&whist[f], 256u);
+          } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              if (cand[c]) atomicAdd(&whist[dp[c]], 1u);
           }
         }
       } else if (dense) {
